@@ -1,0 +1,27 @@
+"""Compile the CPU oracle (oracle.c) into oracle/liboracle.so with gcc.
+
+Test infrastructure only: the oracle checks the HIP library, it is never
+part of it.  Flags: -ffp-contract=off and no -ffast-math, so the C compiler
+keeps every fp64/fp32 operation as written.
+"""
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+
+def build(verbose: bool = False) -> str:
+    cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-ffp-contract=off",
+           "-fno-fast-math", "-fPIC", "-shared", "-Wall", "-Wextra",
+           SRC, "-o", LIB + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))
