@@ -1,0 +1,242 @@
+"""Throughput of the tensor-parallel Linear hot path on one MI355X.
+
+A step is one pass of the path over one batch of synthetic input.  The
+default workload is the Llama-8B MLP tensor-parallel shard: M = 4096 tokens,
+hidden 4096, intermediate 14336, P = 8 shards resident on one GPU:
+  fc1  column-parallel  X [4096, 4096]  x W1 [28672, 4096]^T -> Y1 [4096, 28672]
+  fc2  row-parallel     X2 [4096, 14336] x W2 [4096, 14336]^T -> 8 fp32 partials
+  fold ascending-shard sum of the 8 partials -> Y2 [4096, 4096] bf16
+(tp_linear_column, tp_linear_row with TP_ROW_PARTIAL, tp_shard_reduce: the
+same kernels TP_ROW_SUM runs, called separately so each is timed).
+
+Prints ONE JSON line.  `value` is the step's GEMM TFLOP/s; `roofline` is for
+the dominant kernel (the fc1 column GEMM, MFMA-bound), its time measured with
+HIP events on the stream it runs on; `cpu_baseline` times the CPU oracle on a
+bounded sample of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload 2|3|4|5]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "TFLOP/s and % bf16 MFMA peak, TP column/row Linear shard GEMM; reduce GB/s"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 flop/clk/CU, dense
+PEAK_HBM_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--cpu-rows", type=int, default=2048,
+                    help="rows of X the CPU oracle baseline computes")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+class Workload:
+    """Device buffers and the step for one workload."""
+
+    def __init__(self, wid, torch, tl, synth):
+        self.wid, self.torch, self.tl = wid, torch, tl
+        dev = "cuda:0"
+        P = 8
+        self.P = P
+        sx, sw = synth.SIGMA_X, synth.SIGMA_W
+        nb = lambda g, t, shape, s: synth.device_normal_bf16(synth.seed_for(wid, g, t), shape, s, dev)
+        bf = torch.bfloat16
+        if wid in (2, 3):
+            M, K1, N1, K2, N2 = {2: (4096, 4096, 28672, 14336, 4096),
+                                 3: (8192, 8192, 10240, 8192, 8192)}[wid]
+            self.X1, self.W1 = nb(0, 0, (M, K1), sx), nb(0, 1, (N1, K1), sw)
+            self.X2, self.W2 = nb(1, 0, (M, K2), sx), nb(1, 1, (N2, K2), sw)
+            self.Y1 = torch.empty((M, N1), dtype=bf, device=dev)
+            self.parts = torch.empty((P, M, N2), dtype=torch.float32, device=dev)
+            self.Y2 = torch.empty((M, N2), dtype=bf, device=dev)
+            self.ops = [
+                ("column_gemm", 2.0 * M * N1 * K1, None,
+                 lambda: tl.tp_linear_column(self.X1, self.W1, self.Y1, P)),
+                ("row_gemm", 2.0 * M * N2 * K2, None,
+                 lambda: tl.tp_linear_row(self.X2, self.W2, self.parts, P, tl.TP_ROW_PARTIAL)),
+                ("shard_fold", 0.0, P * M * N2 * 4 + M * N2 * 2,
+                 lambda: tl.tp_shard_reduce(self.parts, self.Y2, P)),
+            ]
+            self.name = {2: "Llama-8B MLP TP shard: M=4096, hidden 4096, intermediate 14336, "
+                            "P=8; fc1 column 4096->28672, fc2 row 14336->4096 + shard fold",
+                         3: "Llama-70B attention TP shard: M=8192, hidden 8192, P=8; QKV column "
+                            "8192->10240, O row 8192->8192 + shard fold"}[wid]
+            self.shape = dict(M=M, K1=K1, N1=N1, K2=K2, N2=N2, P=P)
+        elif wid == 4:
+            M, H, I = 16, 8192, 28672
+            self.X1, self.W1 = nb(0, 0, (M, H), sx), nb(0, 1, (I, H), sw)
+            self.X2, self.W2 = nb(1, 0, (M, I), sx), nb(1, 1, (H, I), sw)
+            self.Y1 = torch.empty((M, I), dtype=bf, device=dev)
+            self.Y2 = torch.empty((M, H), dtype=bf, device=dev)
+            nbytes = tl.tp_row_workspace_bytes(tl.TP_ROW_FUSED, M, H, P)
+            self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+            tl.tp_workspace_zero(self.ws)
+            w1b = I * H * 2 + M * H * 2 + M * I * 2
+            w2b = H * I * 2 + M * I * 2 + M * H * 2
+            self.ops = [
+                ("column_gemm_decode", 2.0 * M * I * H, w1b,
+                 lambda: tl.tp_linear_column(self.X1, self.W1, self.Y1, P)),
+                ("row_gemm_fused_fold", 2.0 * M * H * I, w2b,
+                 lambda: tl.tp_linear_row(self.X2, self.W2, self.Y2, P, tl.TP_ROW_FUSED, self.ws)),
+            ]
+            self.name = "decode M=16, hidden 8192, intermediate 28672, P=8; column fc1 + " \
+                        "row fc2 with the fold fused into the GEMM epilogue"
+            self.shape = dict(M=M, hidden=H, intermediate=I, P=P)
+        else:
+            M, K, N, N3 = 16384, 28672, 8192, 28672
+            self.X1, self.W1 = nb(0, 0, (M, K), sx), nb(0, 1, (N, K), sw)
+            self.W3 = nb(1, 1, (N3, N), sw)
+            self.parts = torch.empty((P, M, N), dtype=torch.float32, device=dev)
+            self.Y = torch.empty((M, N), dtype=bf, device=dev)   # slices = row blocks
+            self.Y3 = torch.empty((M, N3), dtype=bf, device=dev)
+            self.ops = [
+                ("row_gemm", 2.0 * M * N * K, None,
+                 lambda: tl.tp_linear_row(self.X1, self.W1, self.parts, P, tl.TP_ROW_PARTIAL)),
+                ("reduce_scatter_fold", 0.0, P * M * N * 4 + M * N * 2,
+                 lambda: tl.tp_shard_reduce(self.parts, self.Y, P, scatter=1)),
+                ("column_gemm_allgathered", 2.0 * M * N3 * N, None,
+                 lambda: tl.tp_linear_column(self.Y, self.W3, self.Y3, P)),
+            ]
+            self.name = "sequence-parallel: M=16384, K=28672 split P=8, N=8192; row GEMM, " \
+                        "reduce-scatter over tokens, all-gather view -> column 8192->28672"
+            self.shape = dict(M=M, K=K, N=N, N_next=N3, P=P)
+        self.flops = sum(op[1] for op in self.ops)
+
+
+def cpu_baseline(wl, rows, np, oracle, torch):
+    """Time the oracle on the first `rows` token rows of the workload's GEMMs
+    (all output columns), plus the fp32 fold over the same rows."""
+    def host64(t):
+        return oracle.widen_bf16(t.detach().cpu().view(torch.int16).numpy().view(np.uint16))
+    P = wl.P
+    flops, secs, parity = 0.0, 0.0, {}
+    for name, fl, _, _ in wl.ops:
+        if name in ("column_gemm", "column_gemm_decode"):
+            X, W = wl.X1, wl.W1
+            r = min(rows, X.shape[0])
+            X64, Wio = host64(X[:r]), np.ascontiguousarray(host64(W).T)
+            t0 = time.perf_counter()
+            Y = oracle.column_parallel_linear(X64, Wio, P)
+            secs += time.perf_counter() - t0
+            flops += fl * r / X.shape[0]
+            got = host64(wl.Y1[:r])
+            parity[name] = dict(rows=r, rel_l2=oracle.rel_l2(got, Y),
+                                max_abs=oracle.max_abs(got, Y))
+        elif name in ("row_gemm", "row_gemm_fused_fold"):
+            X, W = (wl.X2, wl.W2) if wl.wid != 5 else (wl.X1, wl.W1)
+            r = min(rows, X.shape[0])
+            X64, Wio = host64(X[:r]), np.ascontiguousarray(host64(W).T)
+            t0 = time.perf_counter()
+            parts = oracle.row_partials(X64, Wio, P)
+            Y = oracle.fold_f64(parts)
+            secs += time.perf_counter() - t0
+            flops += fl * r / X.shape[0]
+            out = {2: "Y2", 3: "Y2", 4: "Y2", 5: "Y"}[wl.wid]
+            got = host64(getattr(wl, out)[:r])
+            parity[name] = dict(rows=r, rel_l2=oracle.rel_l2(got, Y),
+                                max_abs=oracle.max_abs(got, Y))
+    return dict(value=flops / secs / 1e12 if secs > 0 else None, unit="TFLOP/s",
+                cores=oracle.num_threads(), kind="oracle",
+                sample=f"first {rows} token rows of each GEMM (all output columns, all K), "
+                       f"fp64 triple loop with explicit shard split/concat/sum; "
+                       f"{flops / 1e9:.1f} GFLOP in {secs:.1f} s"), parity
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: all P shards are resident on one MI355X; "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import synth
+    import tensor_linear_amd as tl
+
+    wl = Workload(args.workload, torch, tl, synth)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        for op in wl.ops:
+            op[3]()
+    torch.cuda.synchronize()
+
+    nops = len(wl.ops)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nops + 1)]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        evs[s][0].record()
+        for i, op in enumerate(wl.ops):
+            op[3]()
+            evs[s][i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall / args.steps * 1e3
+
+    op_stats = {}
+    for i, (name, fl, nbytes, _) in enumerate(wl.ops):
+        ts = sorted(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps))
+        avg = sum(ts) / len(ts)
+        st = dict(avg_us=avg * 1e3, min_us=ts[0] * 1e3, median_us=ts[len(ts) // 2] * 1e3)
+        if fl:
+            st["tflops"] = fl / (avg * 1e-3) / 1e12
+            st["frac_bf16_peak"] = st["tflops"] / PEAK_BF16_TFLOPS
+        if nbytes:
+            st["algorithmic_bytes"] = nbytes
+            st["gbps"] = nbytes / (avg * 1e-3) / 1e9
+            st["frac_hbm_peak"] = st["gbps"] / PEAK_HBM_GBPS
+        op_stats[name] = st
+
+    # dominant kernel: the op with the most time
+    dom = max(op_stats, key=lambda k: op_stats[k]["avg_us"])
+    d = op_stats[dom]
+    if "tflops" in d and wl.wid != 4:
+        roof = dict(kernel=dom, bound="mfma", achieved=d["tflops"], peak=PEAK_BF16_TFLOPS,
+                    unit="TFLOP/s", frac=d["tflops"] / PEAK_BF16_TFLOPS, traffic=None,
+                    avg_launch_us=d["avg_us"])
+    else:
+        roof = dict(kernel=dom, bound="hbm", achieved=d["gbps"], peak=PEAK_HBM_GBPS,
+                    unit="GB/s", frac=d["gbps"] / PEAK_HBM_GBPS, traffic=None,
+                    avg_launch_us=d["avg_us"])
+
+    out = {
+        "metric": METRIC,
+        "value": wl.flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: X ~ N(0,1), W ~ N(0,0.02^2), bf16, drawn on the GPU from fixed seeds",
+        "config": dict(workload=wl.name, **wl.shape),
+        "roofline": roof,
+        "ops": op_stats,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        cb, parity = cpu_baseline(wl, args.cpu_rows, np, oracle, torch)
+        out["cpu_baseline"] = cb
+        out["parity_sample"] = parity
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -13,7 +13,7 @@ LIB = os.path.join(HERE, "liboracle.so")
 
 
 def build(verbose: bool = False) -> str:
-    cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-ffp-contract=off",
+    cmd = ["gcc", "-O3", "-std=c99", "-fopenmp", "-ffp-contract=off",
            "-fno-fast-math", "-fPIC", "-shared", "-Wall", "-Wextra",
            SRC, "-o", LIB + ".tmp"]
     if verbose:

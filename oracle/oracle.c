@@ -14,7 +14,7 @@
  *   - "DTensor API 文档" (MindSpore hyper-parallel), section "reduce_partial":
  *     a Partial value is turned into the reduced value by summing the parts.
  *
- * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (no -ffast-math),
+ * Build: gcc -O3 -fopenmp -ffp-contract=off -fPIC -shared (no -ffast-math),
  * so every add and multiply below is one IEEE operation in the written order.
  *
  * Precision: products of two fp32 (or bf16) numbers are exact in fp64 and

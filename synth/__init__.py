@@ -73,3 +73,16 @@ WORKLOADS = {
             gemms=[("row_scatter", 16384, 28672, 8192, 8),
                    ("column", 16384, 8192, 28672, 8)], dtype="bf16"),
 }
+
+
+def device_normal_bf16(seed: int, shape, sigma: float, device="cuda:0"):
+    """N(0, sigma^2) bf16 tensor drawn on the GPU with torch's seeded
+    generator (used where only throughput is measured and the inputs are too
+    large to draw on the host quickly)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if sigma != 1.0:
+        t.mul_(sigma)
+    return t.to(torch.bfloat16)

@@ -1,0 +1,238 @@
+"""Python binding of libtplinear (include/tplinear.h), the tensor-parallel
+Linear Y = X W on one MI355X with all P shards resident.
+
+Argument marshalling only: every function passes device pointers, sizes and
+leading dimensions taken from torch tensors to the C entry point of the same
+name and turns a non-zero status into an exception (ValueError for argument
+errors, RuntimeError for TP_ERR_HIP).  All arithmetic runs in the HIP
+kernels of the library; there is no fallback.  The first call raises
+ImportError if libtplinear.so has not been built
+(python -m tensor_linear_amd.build).
+
+Tensors: 2-D row-major views with unit column stride; the row stride is the
+leading dimension.  X is [M, K], W is stored [N, K] ([out, in]), Y is [M, N].
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtplinear.so")
+
+_lib = None
+
+
+def _get_lib():
+    """Load libtplinear.so once; fail loudly if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m tensor_linear_amd.build` "
+            "(hipcc, gfx950)")
+    _lib = _declare(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def __getattr__(name):
+    if name == "lib":
+        return _get_lib()
+    raise AttributeError(name)
+
+
+# ---- constants (mirror include/tplinear.h) --------------------------------
+TP_OK, TP_ERR_NULL, TP_ERR_SHAPE, TP_ERR_INDIVISIBLE, TP_ERR_PLACEMENT, \
+    TP_ERR_DTYPE, TP_ERR_MODE, TP_ERR_WORKSPACE, TP_ERR_HIP = range(9)
+TP_F32, TP_BF16 = 0, 1
+TP_REPLICATE, TP_SHARD, TP_PARTIAL = 0, 1, 2
+TP_Y_CONCAT, TP_Y_SHARDS = 0, 1
+TP_ROW_PARTIAL, TP_ROW_SUM, TP_ROW_FUSED, TP_ROW_SCATTER = 0, 1, 2, 3
+TP_MAX_SHARDS = 64
+
+EXPORTS = ("tp_shard_layout", "tp_linear_column", "tp_linear_row", "tp_shard_reduce",
+           "tp_row_workspace_bytes", "tp_workspace_zero", "tp_status_str", "tp_version")
+
+
+class tp_placement(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("dim", ctypes.c_int32)]
+
+
+class tp_view(ctypes.Structure):
+    _fields_ = [("elem_offset", ctypes.c_int64), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("ld", ctypes.c_int64),
+                ("row0", ctypes.c_int64), ("col0", ctypes.c_int64)]
+
+
+_i32, _i64, _ptr, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+
+
+def _declare(lib):
+    lib.tp_shard_layout.argtypes = [_i64, _i64, _i64, tp_placement, _i32, ctypes.POINTER(tp_view)]
+    lib.tp_shard_layout.restype = _i32
+    lib.tp_linear_column.argtypes = [_ptr, _i64, _ptr, _i64, _ptr, _i64, _i32, _i64, _i64, _i64,
+                                     _i32, _i32, _ptr]
+    lib.tp_linear_column.restype = _i32
+    lib.tp_linear_row.argtypes = [_ptr, _i64, _ptr, _i64, _ptr, _i64, _i64, _i32, _ptr, _sz,
+                                  _i64, _i64, _i64, _i32, _i32, _ptr]
+    lib.tp_linear_row.restype = _i32
+    lib.tp_shard_reduce.argtypes = [_ptr, _i64, _i64, _ptr, _i64, _i64, _i32, _i64, _i64, _i32,
+                                    _i32, _ptr]
+    lib.tp_shard_reduce.restype = _i32
+    lib.tp_row_workspace_bytes.argtypes = [_i32, _i64, _i64, _i32]
+    lib.tp_row_workspace_bytes.restype = _sz
+    lib.tp_workspace_zero.argtypes = [_ptr, _sz, _ptr]
+    lib.tp_workspace_zero.restype = _i32
+    lib.tp_status_str.argtypes = [_i32]
+    lib.tp_status_str.restype = ctypes.c_char_p
+    lib.tp_version.argtypes = []
+    lib.tp_version.restype = _i32
+    return lib
+
+
+class TPError(ValueError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(_get_lib().tp_status_str(status).decode())
+
+
+class TPHipError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(_get_lib().tp_status_str(status).decode())
+
+
+def check(status: int) -> None:
+    if status == TP_OK:
+        return
+    if status == TP_ERR_HIP:
+        raise TPHipError(status)
+    raise TPError(status)
+
+
+def tp_status_str(status: int) -> str:
+    return _get_lib().tp_status_str(status).decode()
+
+
+def tp_version() -> int:
+    return int(_get_lib().tp_version())
+
+
+# ---- marshalling helpers --------------------------------------------------
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return TP_BF16
+    if t.dtype == torch.float32:
+        return TP_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: bfloat16 or float32")
+
+
+def _mat(t, name):
+    """(data pointer, rows, cols, leading dim) of a 2-D unit-column-stride view."""
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride")
+    ld = t.stride(0) if t.shape[0] > 1 else max(t.shape[1], 1)
+    return t.data_ptr(), t.shape[0], t.shape[1], max(ld, t.shape[1], 1)
+
+
+def _stream(t, stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    import torch
+    if t.is_cuda:
+        return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    return ctypes.c_void_p(0)
+
+
+# ---- entry points ---------------------------------------------------------
+
+def tp_shard_layout(rows: int, cols: int, ld: int, kind: int, dim: int, P: int) -> list:
+    """Views of the P shards as (elem_offset, rows, cols, ld, row0, col0)."""
+    if not 1 <= P <= TP_MAX_SHARDS:
+        check(TP_ERR_SHAPE)
+    views = (tp_view * P)()
+    check(_get_lib().tp_shard_layout(rows, cols, ld, tp_placement(kind, dim), P, views))
+    return [(v.elem_offset, v.rows, v.cols, v.ld, v.row0, v.col0) for v in views]
+
+
+def tp_linear_column(X, W, Y, P: int, y_mode: int = TP_Y_CONCAT, stream=None) -> None:
+    """Column-parallel Linear.  X [M, K], W [N, K]; Y [M, N] for TP_Y_CONCAT
+    or [P, M, N/P] (block stride M*ldy) for TP_Y_SHARDS."""
+    xp, M, K, ldx = _mat(X, "X")
+    wp, N, Kw, ldw = _mat(W, "W")
+    if Kw != K:
+        raise ValueError(f"X has K={K} but W has K={Kw}")
+    dt = _dtype_code(X)
+    if _dtype_code(W) != dt or _dtype_code(Y) != dt:
+        raise TypeError("X, W and Y must share one dtype")
+    if y_mode == TP_Y_SHARDS:
+        if Y.dim() != 3 or Y.shape[0] != P or Y.shape[1] != M:
+            raise ValueError("Y must be [P, M, N/P] for TP_Y_SHARDS")
+        yp, _, _, ldy = _mat(Y[0], "Y[0]")
+        if P > 1 and Y.stride(0) != M * ldy:
+            raise ValueError("Y blocks must be M*ldy elements apart")
+        yp = Y.data_ptr()
+    else:
+        yp, _, _, ldy = _mat(Y, "Y")
+    check(_get_lib().tp_linear_column(xp, ldx, wp, ldw, yp, ldy, y_mode, M, N, K, P, dt,
+                               _stream(X, stream)))
+
+
+def tp_row_workspace_bytes(mode: int, M: int, N: int, P: int) -> int:
+    return int(_get_lib().tp_row_workspace_bytes(mode, M, N, P))
+
+
+def tp_workspace_zero(buf, stream=None) -> None:
+    check(_get_lib().tp_workspace_zero(buf.data_ptr(), buf.numel() * buf.element_size(),
+                                _stream(buf, stream)))
+
+
+def tp_linear_row(X, W, Y, P: int, mode: int = TP_ROW_SUM, workspace=None,
+                  y_slice_stride: int = 0, stream=None) -> None:
+    """Row-parallel Linear.  X [M, K], W [N, K].  Y: TP_ROW_PARTIAL ->
+    float32 [P, M, N]; TP_ROW_SUM / TP_ROW_FUSED -> [M, N]; TP_ROW_SCATTER ->
+    [M, N] whose row blocks are the slices (y_slice_stride = 0), or a buffer
+    with slice j at element offset j*y_slice_stride and rows [:M/P] of its
+    2-D view Y."""
+    xp, M, K, ldx = _mat(X, "X")
+    wp, N, Kw, ldw = _mat(W, "W")
+    if Kw != K:
+        raise ValueError(f"X has K={K} but W has K={Kw}")
+    dt = _dtype_code(X)
+    if _dtype_code(W) != dt:
+        raise TypeError("X and W must share one dtype")
+    if mode == TP_ROW_PARTIAL:
+        import torch
+        if Y.dtype != torch.float32 or Y.dim() != 3 or Y.shape[0] != P:
+            raise ValueError("Y must be float32 [P, M, N] for TP_ROW_PARTIAL")
+        _, _, _, ldy = _mat(Y[0], "Y[0]")
+        if P > 1 and Y.stride(0) != M * ldy:
+            raise ValueError("Y parts must be M*ldy elements apart")
+        yp = Y.data_ptr()
+    else:
+        if _dtype_code(Y) != dt:
+            raise TypeError("Y must have the dtype of X")
+        yp, _, _, ldy = _mat(Y, "Y")
+    if workspace is not None:
+        wsp, wsb = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    else:
+        wsp, wsb = None, 0
+    check(_get_lib().tp_linear_row(xp, ldx, wp, ldw, yp, ldy, y_slice_stride, mode, wsp, wsb,
+                            M, N, K, P, dt, _stream(X, stream)))
+
+
+def tp_shard_reduce(partials, Y, P: int, scatter: int = 0, y_slice_stride: int = 0,
+                    stream=None) -> None:
+    """Fold float32 partials [P, M, N] (or any [P, M, ldp] view) into Y [M, N]
+    (scatter=0) or into P token slices (scatter=1)."""
+    import torch
+    if partials.dtype != torch.float32 or partials.dim() != 3 or partials.shape[0] != P:
+        raise ValueError("partials must be float32 [P, M, N]")
+    _, M, N, ldp = _mat(partials[0], "partials[0]")
+    ss = partials.stride(0) if P > 1 else M * ldp
+    yp, _, _, ldy = _mat(Y, "Y")
+    check(_get_lib().tp_shard_reduce(partials.data_ptr(), ss, ldp, yp, ldy, y_slice_stride, scatter,
+                              M, N, P, _dtype_code(Y), _stream(partials, stream)))

@@ -1,0 +1,232 @@
+// Host side of libtplinear: argument checks, the placement -> view map and
+// the choice of kernel for each shard GEMM.  Declarations and the meaning of
+// every argument are in include/tplinear.h.
+#include "tplinear.h"
+
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+namespace {
+
+using namespace tpl;
+
+constexpr size_t WS_ALIGN = 256;
+
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+inline bool valid_dtype(int32_t d) { return d == TP_F32 || d == TP_BF16; }
+
+inline tp_status hip_status(hipError_t e) { return e == hipSuccess ? TP_OK : TP_ERR_HIP; }
+
+// Common size checks of the two Linear entry points.
+tp_status check_gemm_shape(int64_t M, int64_t N, int64_t K, int32_t P, int64_t ldx,
+                           int64_t ldw) {
+    if (M < 0 || N < 0 || K < 0) return TP_ERR_SHAPE;
+    if (P < 1 || P > TP_MAX_SHARDS) return TP_ERR_SHAPE;
+    if (ldx < K || ldw < K || ldx < 1 || ldw < 1) return TP_ERR_SHAPE;
+    return TP_OK;
+}
+
+// Run one grouped shard GEMM with the best kernel that takes it.
+// Decode-shaped bf16 problems (M <= 64) stream W with the skinny kernel;
+// large aligned bf16 problems use the 256x256 MFMA tile kernel; everything
+// else (fp32, odd K, unaligned views) uses the generic kernel.
+hipError_t run_gemm(const GemmArgs &g, int32_t dtype, int out_type, hipStream_t s) {
+    if (dtype == TP_BF16) {
+        if (gemm_skinny_supported(g)) return launch_gemm_skinny(g, out_type, nullptr, s);
+        if (gemm_tile_supported(g)) return launch_gemm_tile(g, out_type, s);
+        return launch_gemm_generic(g, IN_BF16, out_type, s);
+    }
+    return launch_gemm_generic(g, IN_F32, out_type, s);
+}
+
+size_t partials_bytes(int64_t M, int64_t N, int32_t P) {
+    return round_up((size_t)P * (size_t)M * (size_t)N * sizeof(float), WS_ALIGN);
+}
+
+size_t counters_bytes(int64_t N) {
+    const size_t tiles = (size_t)((N + SKINNY_BN - 1) / SKINNY_BN);
+    return round_up(tiles * sizeof(uint32_t), WS_ALIGN);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t tp_version(void) { return 100; }
+
+const char *tp_status_str(int32_t s) {
+    switch (s) {
+        case TP_OK: return "TP_OK";
+        case TP_ERR_NULL: return "TP_ERR_NULL: a required pointer is NULL";
+        case TP_ERR_SHAPE: return "TP_ERR_SHAPE: invalid size, leading dimension or shard count";
+        case TP_ERR_INDIVISIBLE: return "TP_ERR_INDIVISIBLE: the split dimension is not a multiple of P";
+        case TP_ERR_PLACEMENT: return "TP_ERR_PLACEMENT: invalid placement kind or dim";
+        case TP_ERR_DTYPE: return "TP_ERR_DTYPE: invalid dtype";
+        case TP_ERR_MODE: return "TP_ERR_MODE: invalid mode";
+        case TP_ERR_WORKSPACE: return "TP_ERR_WORKSPACE: workspace missing or too small";
+        case TP_ERR_HIP: return "TP_ERR_HIP: a HIP call or kernel launch failed";
+        default: return "unknown tp_status";
+    }
+}
+
+tp_status tp_shard_layout(int64_t rows, int64_t cols, int64_t ld, tp_placement pl, int32_t P,
+                          tp_view *views) {
+    if (!views) return TP_ERR_NULL;
+    if (rows < 0 || cols < 0 || ld < cols || P < 1 || P > TP_MAX_SHARDS) return TP_ERR_SHAPE;
+    if (pl.kind == TP_SHARD) {
+        int d = pl.dim;
+        if (d < 0) d += 2;
+        if (d != 0 && d != 1) return TP_ERR_PLACEMENT;
+        const int64_t L = d == 0 ? rows : cols;
+        if (L % P != 0) return TP_ERR_INDIVISIBLE;
+        const int64_t s = L / P;
+        for (int32_t i = 0; i < P; ++i) {
+            tp_view v;
+            v.ld = ld;
+            if (d == 0) {
+                v.row0 = i * s; v.col0 = 0; v.rows = s; v.cols = cols;
+            } else {
+                v.row0 = 0; v.col0 = i * s; v.rows = rows; v.cols = s;
+            }
+            v.elem_offset = v.row0 * ld + v.col0;
+            views[i] = v;
+        }
+        return TP_OK;
+    }
+    if (pl.kind == TP_REPLICATE || pl.kind == TP_PARTIAL) {
+        for (int32_t i = 0; i < P; ++i) {
+            tp_view v;
+            v.ld = ld; v.rows = rows; v.cols = cols; v.row0 = 0; v.col0 = 0;
+            v.elem_offset = pl.kind == TP_PARTIAL ? (int64_t)i * rows * ld : 0;
+            views[i] = v;
+        }
+        return TP_OK;
+    }
+    return TP_ERR_PLACEMENT;
+}
+
+tp_status tp_linear_column(const void *X, int64_t ldx, const void *W, int64_t ldw, void *Y,
+                           int64_t ldy, int32_t y_mode, int64_t M, int64_t N, int64_t K,
+                           int32_t P, int32_t dtype, void *stream) {
+    tp_status st = check_gemm_shape(M, N, K, P, ldx, ldw);
+    if (st != TP_OK) return st;
+    if (!valid_dtype(dtype)) return TP_ERR_DTYPE;
+    if (y_mode != TP_Y_CONCAT && y_mode != TP_Y_SHARDS) return TP_ERR_MODE;
+    if (N % P != 0) return TP_ERR_INDIVISIBLE;
+    const int64_t Ns = N / P;
+    if (y_mode == TP_Y_CONCAT ? ldy < N : ldy < Ns) return TP_ERR_SHAPE;
+    if (ldy < 1) return TP_ERR_SHAPE;
+    if (M == 0 || N == 0) return TP_OK;
+    if (!Y || (K > 0 && (!X || !W))) return TP_ERR_NULL;
+
+    GemmArgs g;
+    g.A = X; g.lda = ldx; g.a_shard = 0;
+    g.B = W; g.ldb = ldw; g.b_shard = Ns * ldw;
+    g.C = Y; g.ldc = ldy; g.c_shard = y_mode == TP_Y_CONCAT ? Ns : M * ldy;
+    g.M = M; g.N = Ns; g.K = K; g.P = P;
+    const int out = dtype == TP_BF16 ? OUT_BF16 : OUT_F32;
+    return hip_status(run_gemm(g, dtype, out, (hipStream_t)stream));
+}
+
+size_t tp_row_workspace_bytes(int32_t mode, int64_t M, int64_t N, int32_t P) {
+    if (M < 0 || N < 0 || P < 1 || P > TP_MAX_SHARDS) return 0;
+    switch (mode) {
+        case TP_ROW_SUM:
+        case TP_ROW_SCATTER: return partials_bytes(M, N, P);
+        case TP_ROW_FUSED: return partials_bytes(M, N, P) + counters_bytes(N);
+        default: return 0;
+    }
+}
+
+tp_status tp_linear_row(const void *X, int64_t ldx, const void *W, int64_t ldw, void *Y,
+                        int64_t ldy, int64_t y_slice_stride, int32_t mode, void *workspace,
+                        size_t ws_bytes, int64_t M, int64_t N, int64_t K, int32_t P,
+                        int32_t dtype, void *stream) {
+    tp_status st = check_gemm_shape(M, N, K, P, ldx, ldw);
+    if (st != TP_OK) return st;
+    if (!valid_dtype(dtype)) return TP_ERR_DTYPE;
+    if (mode < TP_ROW_PARTIAL || mode > TP_ROW_SCATTER) return TP_ERR_MODE;
+    if (K % P != 0) return TP_ERR_INDIVISIBLE;
+    if (mode == TP_ROW_SCATTER && M % P != 0) return TP_ERR_INDIVISIBLE;
+    if (ldy < N || ldy < 1) return TP_ERR_SHAPE;
+    if (y_slice_stride < 0) return TP_ERR_SHAPE;
+    if (M == 0 || N == 0) return TP_OK;
+    if (!Y || (K > 0 && (!X || !W))) return TP_ERR_NULL;
+    const size_t need = tp_row_workspace_bytes(mode, M, N, P);
+    if (need > 0 && (!workspace || ws_bytes < need || ((uintptr_t)workspace % WS_ALIGN) != 0))
+        return TP_ERR_WORKSPACE;
+
+    const hipStream_t s = (hipStream_t)stream;
+    const int64_t Ks = K / P;
+    GemmArgs g;
+    g.A = X; g.lda = ldx; g.a_shard = Ks;
+    g.B = W; g.ldb = ldw; g.b_shard = Ks;
+    g.M = M; g.N = N; g.K = Ks; g.P = P;
+    const int out = dtype == TP_BF16 ? OUT_BF16 : OUT_F32;
+
+    if (mode == TP_ROW_PARTIAL) {
+        g.C = Y; g.ldc = ldy; g.c_shard = M * ldy;
+        return hip_status(run_gemm(g, dtype, OUT_F32, s));
+    }
+
+    float *parts = (float *)workspace;
+    g.C = parts; g.ldc = N; g.c_shard = M * N;
+
+    if (mode == TP_ROW_FUSED && dtype == TP_BF16 && gemm_skinny_supported(g)) {
+        FoldArgs f;
+        f.Y = Y; f.ldy = ldy; f.out_type = out;
+        f.partials = parts;
+        f.counters = (uint32_t *)((char *)workspace + partials_bytes(M, N, P));
+        return hip_status(launch_gemm_skinny(g, out, &f, s));
+    }
+
+    hipError_t e = run_gemm(g, dtype, OUT_F32, s);
+    if (e != hipSuccess) return TP_ERR_HIP;
+    ReduceArgs r;
+    r.partials = parts; r.shard_stride = M * N; r.ldp = N;
+    r.Y = Y; r.ldy = ldy; r.M = M; r.N = N; r.P = P;
+    if (mode == TP_ROW_SCATTER) {
+        r.slice_rows = M / P;
+        r.slice_stride = y_slice_stride ? y_slice_stride : (M / P) * ldy;
+    } else {
+        r.slice_rows = M;
+        r.slice_stride = 0;
+    }
+    return hip_status(launch_shard_fold(r, out, s));
+}
+
+tp_status tp_shard_reduce(const float *partials, int64_t shard_stride, int64_t ldp, void *Y,
+                          int64_t ldy, int64_t y_slice_stride, int32_t scatter, int64_t M,
+                          int64_t N, int32_t P, int32_t out_dtype, void *stream) {
+    if (M < 0 || N < 0 || P < 1 || P > TP_MAX_SHARDS) return TP_ERR_SHAPE;
+    if (ldp < N || ldy < N || ldp < 1 || ldy < 1 || shard_stride < 0 || y_slice_stride < 0)
+        return TP_ERR_SHAPE;
+    if (!valid_dtype(out_dtype)) return TP_ERR_DTYPE;
+    if (scatter != 0 && scatter != 1) return TP_ERR_MODE;
+    if (scatter && M % P != 0) return TP_ERR_INDIVISIBLE;
+    if (M == 0 || N == 0) return TP_OK;
+    if (!partials || !Y) return TP_ERR_NULL;
+    ReduceArgs r;
+    r.partials = partials; r.shard_stride = shard_stride; r.ldp = ldp;
+    r.Y = Y; r.ldy = ldy; r.M = M; r.N = N; r.P = P;
+    if (scatter) {
+        r.slice_rows = M / P;
+        r.slice_stride = y_slice_stride ? y_slice_stride : (M / P) * ldy;
+    } else {
+        r.slice_rows = M;
+        r.slice_stride = 0;
+    }
+    return hip_status(launch_shard_fold(r, out_dtype == TP_BF16 ? OUT_BF16 : OUT_F32,
+                                        (hipStream_t)stream));
+}
+
+tp_status tp_workspace_zero(void *ptr, size_t bytes, void *stream) {
+    if (bytes == 0) return TP_OK;
+    if (!ptr) return TP_ERR_NULL;
+    if (bytes % 4 != 0 || ((uintptr_t)ptr % 4) != 0) return TP_ERR_SHAPE;
+    return hip_status(launch_fill_zero(ptr, bytes / 4, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -8,3 +8,9 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+    # Build the HIP library only when nothing is built yet (a fresh checkout);
+    # an existing build is used as it is.
+    lib = os.path.join(ROOT, "tensor_linear_amd", "libtplinear.so")
+    if not os.path.exists(lib):
+        from tensor_linear_amd import build as _b
+        _b.build()

@@ -1,0 +1,187 @@
+"""CPU tests of the C ABI: the library loads without a GPU, exports every
+function include/tplinear.h declares, maps placements to views exactly as
+the oracle's integer index maps do, and rejects every bad argument on the
+host before queuing any GPU work.  No call here reaches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+import tensor_linear_amd as tl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    with open(os.path.join(ROOT, "include", "tplinear.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tp_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported():
+    declared = _declared_functions()
+    assert set(declared) == set(tl.EXPORTS)
+    lib = ctypes.CDLL(tl.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for s in range(9):
+        assert tl.tp_status_str(s).startswith("TP_")
+    assert "unknown" in tl.tp_status_str(99)
+    assert tl.tp_version() >= 100
+
+
+# ---- tp_shard_layout against the oracle's index maps (bit-exact) ----------
+
+@pytest.mark.parametrize("R,C,extra", [(1, 1, 0), (4, 4, 0), (6, 10, 3), (8, 3, 1),
+                                       (12, 12, 5), (16, 64, 0)])
+def test_layout_matches_oracle(R, C, extra):
+    ld = C + extra
+    for kind in (tl.TP_SHARD, tl.TP_REPLICATE, tl.TP_PARTIAL):
+        dims = (0, 1, -1, -2) if kind == tl.TP_SHARD else (0,)
+        for dim in dims:
+            L = R if dim in (0, -2) else C
+            for P in range(1, min(L, 16) + 1):
+                if kind == tl.TP_SHARD and L % P:
+                    with pytest.raises(tl.TPError) as e:
+                        tl.tp_shard_layout(R, C, ld, kind, dim, P)
+                    assert e.value.status == tl.TP_ERR_INDIVISIBLE
+                    continue
+                got = tl.tp_shard_layout(R, C, ld, kind, dim, P)
+                want = oracle.expected_views(R, C, ld, kind, dim, P)
+                assert got == want, (kind, dim, P)
+
+
+def test_layout_printed_example():
+    # DTensor API page, distribute_tensor: 4x4 arange, Shard(0) over 2 ->
+    # rows 0-1 and rows 2-3.
+    import numpy as np
+    A = np.arange(16).reshape(4, 4)
+    views = tl.tp_shard_layout(4, 4, 4, tl.TP_SHARD, 0, 2)
+    flat = A.reshape(-1)
+    got = [flat[off:off + r * ld].reshape(r, ld)[:, :c] for off, r, c, ld, _, _ in views]
+    assert np.array_equal(got[0], [[0, 1, 2, 3], [4, 5, 6, 7]])
+    assert np.array_equal(got[1], [[8, 9, 10, 11], [12, 13, 14, 15]])
+    # weight (1024, 4096), Shard(1) over 4 -> (1024, 1024) each
+    assert all((r, c) == (1024, 1024) for _, r, c, _, _, _ in
+               tl.tp_shard_layout(1024, 4096, 4096, tl.TP_SHARD, 1, 4))
+
+
+def test_layout_errors():
+    lib = tl.lib
+    views = (tl.tp_view * 4)()
+    pl = tl.tp_placement(tl.TP_SHARD, 0)
+    assert lib.tp_shard_layout(4, 4, 4, pl, 2, None) == tl.TP_ERR_NULL
+    assert lib.tp_shard_layout(-1, 4, 4, pl, 2, views) == tl.TP_ERR_SHAPE
+    assert lib.tp_shard_layout(4, 4, 3, pl, 2, views) == tl.TP_ERR_SHAPE
+    assert lib.tp_shard_layout(4, 4, 4, pl, 0, views) == tl.TP_ERR_SHAPE
+    assert lib.tp_shard_layout(4, 4, 4, pl, 65, views) == tl.TP_ERR_SHAPE
+    assert lib.tp_shard_layout(4, 4, 4, tl.tp_placement(7, 0), 2, views) == tl.TP_ERR_PLACEMENT
+    assert lib.tp_shard_layout(4, 4, 4, tl.tp_placement(tl.TP_SHARD, 2), 2, views) == \
+        tl.TP_ERR_PLACEMENT
+    assert lib.tp_shard_layout(4, 4, 4, tl.tp_placement(tl.TP_SHARD, -3), 2, views) == \
+        tl.TP_ERR_PLACEMENT
+    assert lib.tp_shard_layout(5, 4, 4, pl, 2, views) == tl.TP_ERR_INDIVISIBLE
+    assert lib.tp_shard_layout(0, 0, 0, pl, 4, views) == tl.TP_OK
+
+
+# ---- host-side argument checks of the compute entry points ---------------
+# Fake but non-null addresses: every call below must be rejected (or be an
+# empty problem) before anything is queued, so no address is dereferenced.
+
+FX, FW, FY, FWS = 0x100000, 0x200000, 0x300000, 0x400000
+
+
+def col(**kw):
+    a = dict(X=FX, ldx=8, W=FW, ldw=8, Y=FY, ldy=12, y_mode=tl.TP_Y_CONCAT, M=3, N=12, K=8,
+             P=4, dtype=tl.TP_BF16, stream=None)
+    a.update(kw)
+    return tl.lib.tp_linear_column(a["X"], a["ldx"], a["W"], a["ldw"], a["Y"], a["ldy"],
+                                   a["y_mode"], a["M"], a["N"], a["K"], a["P"], a["dtype"],
+                                   a["stream"])
+
+
+def row(**kw):
+    a = dict(X=FX, ldx=8, W=FW, ldw=8, Y=FY, ldy=12, ss=0, mode=tl.TP_ROW_SUM, ws=FWS,
+             wsb=1 << 20, M=4, N=12, K=8, P=4, dtype=tl.TP_BF16, stream=None)
+    a.update(kw)
+    return tl.lib.tp_linear_row(a["X"], a["ldx"], a["W"], a["ldw"], a["Y"], a["ldy"], a["ss"],
+                                a["mode"], a["ws"], a["wsb"], a["M"], a["N"], a["K"], a["P"],
+                                a["dtype"], a["stream"])
+
+
+def red(**kw):
+    a = dict(p=FWS, ss=48, ldp=12, Y=FY, ldy=12, yss=0, scatter=0, M=4, N=12, P=4,
+             dtype=tl.TP_BF16, stream=None)
+    a.update(kw)
+    return tl.lib.tp_shard_reduce(a["p"], a["ss"], a["ldp"], a["Y"], a["ldy"], a["yss"],
+                                  a["scatter"], a["M"], a["N"], a["P"], a["dtype"], a["stream"])
+
+
+def test_column_errors():
+    assert col(X=None) == tl.TP_ERR_NULL
+    assert col(W=None) == tl.TP_ERR_NULL
+    assert col(Y=None) == tl.TP_ERR_NULL
+    assert col(M=-1) == tl.TP_ERR_SHAPE
+    assert col(K=-1) == tl.TP_ERR_SHAPE
+    assert col(P=0) == tl.TP_ERR_SHAPE
+    assert col(P=65) == tl.TP_ERR_SHAPE
+    assert col(ldx=7) == tl.TP_ERR_SHAPE
+    assert col(ldw=7) == tl.TP_ERR_SHAPE
+    assert col(ldy=11) == tl.TP_ERR_SHAPE                       # concat needs ldy >= N
+    assert col(ldy=2, y_mode=tl.TP_Y_SHARDS) == tl.TP_ERR_SHAPE  # shards need ldy >= N/P
+    assert col(N=10) == tl.TP_ERR_INDIVISIBLE
+    assert col(dtype=2) == tl.TP_ERR_DTYPE
+    assert col(y_mode=5) == tl.TP_ERR_MODE
+    # empty problems are valid and queue nothing
+    assert col(M=0) == tl.TP_OK
+    assert col(N=0) == tl.TP_OK
+    assert col(M=0, X=None, W=None, Y=None) == tl.TP_OK
+
+
+def test_row_errors():
+    need = tl.tp_row_workspace_bytes(tl.TP_ROW_SUM, 4, 12, 4)
+    assert need >= 4 * 4 * 12 * 4
+    assert row(X=None) == tl.TP_ERR_NULL
+    assert row(Y=None) == tl.TP_ERR_NULL
+    assert row(P=0) == tl.TP_ERR_SHAPE
+    assert row(ldy=11) == tl.TP_ERR_SHAPE
+    assert row(ss=-1, mode=tl.TP_ROW_SCATTER) == tl.TP_ERR_SHAPE
+    assert row(K=10, ldx=10, ldw=10) == tl.TP_ERR_INDIVISIBLE
+    assert row(M=6, mode=tl.TP_ROW_SCATTER) == tl.TP_ERR_INDIVISIBLE
+    assert row(dtype=7) == tl.TP_ERR_DTYPE
+    assert row(mode=4) == tl.TP_ERR_MODE
+    assert row(mode=-1) == tl.TP_ERR_MODE
+    assert row(ws=None) == tl.TP_ERR_WORKSPACE
+    assert row(wsb=need - 1) == tl.TP_ERR_WORKSPACE
+    assert row(ws=FWS + 4) == tl.TP_ERR_WORKSPACE              # not 256-byte aligned
+    assert row(mode=tl.TP_ROW_FUSED, wsb=need) == tl.TP_ERR_WORKSPACE  # + counters
+    assert row(M=0) == tl.TP_OK
+    assert tl.tp_row_workspace_bytes(tl.TP_ROW_PARTIAL, 4, 12, 4) == 0
+    assert tl.tp_row_workspace_bytes(tl.TP_ROW_SUM, 4, 12, 0) == 0
+    fused = tl.tp_row_workspace_bytes(tl.TP_ROW_FUSED, 16, 8192, 8)
+    assert fused >= 8 * 16 * 8192 * 4 + (8192 // 64) * 4
+
+
+def test_reduce_errors():
+    assert red(p=None) == tl.TP_ERR_NULL
+    assert red(Y=None) == tl.TP_ERR_NULL
+    assert red(P=0) == tl.TP_ERR_SHAPE
+    assert red(ldp=11) == tl.TP_ERR_SHAPE
+    assert red(ldy=11) == tl.TP_ERR_SHAPE
+    assert red(ss=-1) == tl.TP_ERR_SHAPE
+    assert red(dtype=3) == tl.TP_ERR_DTYPE
+    assert red(scatter=2) == tl.TP_ERR_MODE
+    assert red(scatter=1, M=6) == tl.TP_ERR_INDIVISIBLE
+    assert red(M=0) == tl.TP_OK
+
+
+def test_workspace_zero_errors():
+    assert tl.lib.tp_workspace_zero(None, 16, None) == tl.TP_ERR_NULL
+    assert tl.lib.tp_workspace_zero(FWS, 6, None) == tl.TP_ERR_SHAPE
+    assert tl.lib.tp_workspace_zero(None, 0, None) == tl.TP_OK
