@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="rows of X the CPU oracle baseline computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run 3 device-to-device copies of this many MiB (a plain copy "
+                         "of known size, to scale hardware byte counters)")
     return ap.parse_args()
 
 
@@ -165,6 +168,15 @@ def main():
     import torch
     import synth
     import tensor_linear_amd as tl
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     wl = Workload(args.workload, torch, tl, synth)
     torch.cuda.synchronize()

@@ -122,39 +122,81 @@ void gemm_tile_kernel(GemmArgs g, int tiles_m, int tiles_n, int vec_store) {
     }
 
     // Fragment addressing: a 32x32x16 operand fragment is 32 rows x 16 k;
-    // lane reads row lane%32, k-chunk 2*ks + lane/32 (8 bf16 = 16 bytes).
+    // lane reads row lane%32, k-chunk 2*ks + lane/32 (8 bf16 = 16 bytes),
+    // stored at slot chunk ^ (row & 7) = chunk ^ (lane & 7).
     const int frow = lane & 31;
     const int fhalf = lane >> 5;
-    const int fx = lane & 7;  // row & 7 for every fragment row
+    const int fx = lane & 7;
+    const int wrow_off = (wn * 128 + frow) * 128;
+    const int xrow_off = (wm * 128 + frow) * 128;
 
     for (int kt = 0; kt < nk; ++kt) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (kt + 1 < nk) {
-            const int64_t kb = (int64_t)(kt + 1) * TK * 2;
-            LDS_PTR(char) nxt = lds + ((kt + 1) & 1) * STAGE;
-            issue_tile(Abase + kb, aoff, nxt, wave);
-            issue_tile(Bbase + kb, boff, nxt + OPB, wave);
-        }
         LDS_PTR(char) As = lds + (kt & 1) * STAGE;
         LDS_PTR(char) Bs = As + OPB;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const int slot = ((2 * ks + fhalf) ^ fx) << 4;
-            bf16x8 wf[4], xf[4];
+
+        bf16x8 wf[2][4], xf[2][4];
+        {
+            const int slot = (fhalf ^ fx) << 4;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                wf[i] = *(LDS_PTR(bf16x8))(Bs + (wn * 128 + i * 32 + frow) * 128 + slot);
+                wf[0][i] = *(LDS_PTR(bf16x8))(Bs + wrow_off + i * 4096 + slot);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                xf[j] = *(LDS_PTR(bf16x8))(As + (wm * 128 + j * 32 + frow) * 128 + slot);
+                xf[0][j] = *(LDS_PTR(bf16x8))(As + xrow_off + j * 4096 + slot);
+        }
+        // Phase ks: issue the fragment reads of step ks+1, then the 16
+        // independent MFMAs of step ks, whose operands were read one phase
+        // earlier.  The fences keep the compiler from mixing phases (which
+        // would put dependent MFMAs back to back).
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            __builtin_amdgcn_sched_barrier(0);
+            const int cur = ks & 1, nx = cur ^ 1;
+            if (ks == 0) {
+                // Prefetch the next K step into the idle stage.  The last
+                // step reloads its own K range there instead, so the body
+                // has no branch; that stage is not read again.
+                const int kn = kt + 1 < nk ? kt + 1 : kt;
+                const int64_t kb = (int64_t)kn * TK * 2;
+                LDS_PTR(char) nxt = lds + ((kt + 1) & 1) * STAGE;
+                issue_tile(Abase + kb, aoff, nxt, wave);
+                issue_tile(Bbase + kb, boff, nxt + OPB, wave);
+            }
+            if (ks < 3) {
+                const int slot = ((2 * (ks + 1) + fhalf) ^ fx) << 4;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    wf[nx][i] = *(LDS_PTR(bf16x8))(Bs + wrow_off + i * 4096 + slot);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    xf[nx][j] = *(LDS_PTR(bf16x8))(As + xrow_off + j * 4096 + slot);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], xf[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][i], xf[cur][j],
+                                                                        acc[i][j], 0, 0, 0);
+            // One MFMA first (it consumes the reads of the previous phase, so
+            // the wait for them never also covers the new ones: at most 8
+            // LDS reads are in flight, within what lgkmcnt can count), then
+            // the next step's 8 reads, then the other 15 MFMAs.  Phase 0
+            // first issues the 16 global->LDS loads of the next K step.
+            if (ks == 0) __builtin_amdgcn_sched_group_barrier(0x020, 16, 0);  // VMEM read
+            if (ks < 3) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // DS read
+                __builtin_amdgcn_sched_group_barrier(0x008, 15, 0);
+            } else {
+                __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+            }
         }
+        __builtin_amdgcn_sched_barrier(0);
     }
+    // No global->LDS load may still be writing when the workgroup ends.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // ---- epilogue.  32x32 D layout with W rows as the row operand:
     // lane holds m = lane%32 and, for q = 0..3, the 4 columns
