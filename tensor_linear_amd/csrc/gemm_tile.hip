@@ -3,29 +3,29 @@
 // Y_i = X W_i and the row partials X_i W_i; both operands are K-contiguous in
 // the [N, K] weight storage, so no transpose is needed).
 //
-// Workgroup tile 256 (M) x 256 (N), K step 64, 256 threads = 4 waves in a
-// 2x2 grid, each wave owning a 128x128 block = 4x4 v_mfma_f32_32x32x16_bf16
-// accumulators (256 fp32 registers per lane).  The W tile is the MFMA row
-// operand and the X tile the column operand, so each lane ends up holding
-// 4 consecutive output columns of one row: 16-byte fp32 / 8-byte bf16 stores.
+// Output tile 256 (M) x 256 (N); 256 threads = 4 waves in a 2x2 grid, each
+// wave owning a 128x128 block = 4x4 v_mfma_f32_32x32x16_bf16 accumulators
+// (256 fp32 registers per lane).  The W tile is the MFMA row operand and the
+// X tile the column operand, so each lane holds 4 consecutive output columns
+// of one row: 16-byte fp32 / 8-byte bf16 stores.
 //
-// Global -> LDS: global_load_lds_dwordx4 (16 bytes per lane straight into LDS,
-// no register staging).  One wave instruction fills 1 KB = 8 LDS rows of
-// 128 bytes (64 bf16 of K).  Within a row the 16-byte chunk holding k-chunk c
-// sits at slot c ^ (row & 7); the lanes choose their global addresses to
-// produce that swizzle, so the 32 lanes of a fragment read (32 rows, one
-// chunk each) hit 8 different 16-byte slots per group of 8 rows.
-// Two LDS stages (2 x 64 KB): the loads for step k+1 are in flight while
-// step k is multiplied; one barrier per step.
+// Persistent: one workgroup per CU walks a list of tiles, and the K pipeline
+// runs straight across tile boundaries -- the first K steps of the next tile
+// are loaded while the current tile finishes and writes its outputs -- so no
+// CU sits idle between tiles.  Workgroup b runs on XCD b % 8; the tiles are
+// split into 8 contiguous ranges, one per XCD, and inside a range the 32
+// workgroups of the XCD take consecutive tiles (visited in groups of 8
+// tile-rows), so the panels of X and W they share stay in that XCD's L2.
+//
+// Global -> LDS: global_load_lds_dwordx4 (16 bytes per lane straight into
+// LDS, no register staging), NST stages of BK columns of K.  One wave
+// instruction fills 1 KB of LDS.  Rows are BK*2 bytes; 16-byte chunk c of row
+// r sits at slot c ^ ((r / RP) % CPR) (RP rows per 256 bytes, CPR chunks per
+// row), so the 16 rows read by one 16-lane group of ds_read_b128 hit 16
+// different 16-byte bank groups.
 //
 // Edges: rows past M or N are clamped to the last valid row (their results
-// are not stored).  K must be a multiple of 64; other K go to the generic
-// kernel.
-//
-// Tile order: workgroup b runs on XCD b % 8, so b is remapped to give each
-// XCD a contiguous range of tiles, and tiles inside a shard are visited in
-// groups of 8 tile-rows so the workgroups resident on one XCD share X and W
-// panels in that XCD's L2.
+// are not stored).  K must be a multiple of BK.
 #include "kernels.h"
 
 namespace tpl {
@@ -38,227 +38,361 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_PTR(T) __attribute__((address_space(3))) T *
 
-constexpr int TB = 256;          // tile edge in M and N
-constexpr int TK = 64;           // K per stage
-constexpr int TT = 256;          // threads
-constexpr int OPB = TB * TK * 2; // bytes of one operand tile (32 KB)
-constexpr int STAGE = 2 * OPB;   // A tile + B tile
+constexpr int TB = 256;  // tile edge in M and N
+constexpr int TT = 256;  // threads
 constexpr int GROUP_M = 8;
 
-// Issue the 8 direct-to-LDS loads of this wave for one operand tile.
-// base: the operand's row 0 of this tile at k = k0 (uniform).
-// off[j]: this lane's byte offset for load j (row clamp and swizzle applied).
-__device__ __forceinline__ void issue_tile(const char *base, const uint32_t (&off)[8],
-                                           LDS_PTR(char) dst, int wave) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        __builtin_amdgcn_global_load_lds((const void *)(base + off[j]),
-                                         (LDS_PTR(void))(dst + (j * 4 + wave) * 1024), 16, 0, 0);
-    }
+struct TileSched {
+    int tiles_m, tiles_n;  // per shard
+    int T;                 // tiles over all shards
+    int xcd_split;         // 1: XCD-contiguous ranges (grid == 8 * per_xcd)
+    int per_xcd;           // workgroups per XCD when xcd_split
+};
+
+// Logical tile index -> (shard, tile row, tile column), tile rows grouped by
+// GROUP_M inside a shard.
+__device__ __forceinline__ void decode_tile(const TileSched &ts, int logical, int &shard,
+                                           int &tm, int &tn) {
+    const int per_shard = ts.tiles_m * ts.tiles_n;
+    shard = logical / per_shard;
+    const int t = logical - shard * per_shard;
+    const int in_group = GROUP_M * ts.tiles_n;
+    const int first_m = (t / in_group) * GROUP_M;
+    const int gsz = min(ts.tiles_m - first_m, GROUP_M);
+    const int tr = t - (t / in_group) * in_group;
+    tm = first_m + tr % gsz;
+    tn = tr / gsz;
 }
 
-template <int OUT>
-__global__ __attribute__((amdgpu_flat_work_group_size(TT, TT), amdgpu_waves_per_eu(1, 1)))
-void gemm_tile_kernel(GemmArgs g, int tiles_m, int tiles_n, int vec_store) {
-    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
-
-    // ---- tile index: XCD-contiguous ranges, then grouped order in a shard.
-    const int T = gridDim.x;
+// The q-th tile of this workgroup, or -1 when it has no q-th tile.
+__device__ __forceinline__ int tile_of(const TileSched &ts, int q) {
     const int b = blockIdx.x;
-    const int logical = (T % 8 == 0) ? (b % 8) * (T / 8) + (b / 8) : b;
-    const int per_shard = tiles_m * tiles_n;
-    const int shard = logical / per_shard;
-    const int t = logical - shard * per_shard;
-    const int in_group = GROUP_M * tiles_n;
-    const int first_m = (t / in_group) * GROUP_M;
-    const int gsz = min(tiles_m - first_m, GROUP_M);
-    const int tr = t % in_group;
-    const int tile_m = first_m + tr % gsz;
-    const int tile_n = tr / gsz;
-    const int64_t m0 = (int64_t)tile_m * TB;
-    const int64_t n0 = (int64_t)tile_n * TB;
+    if (ts.xcd_split) {
+        const int x = b & 7, lb = b >> 3;
+        const int per = (ts.T + 7) >> 3;
+        const int lo = x * per, hi = min(lo + per, ts.T);
+        const int t = lo + lb + q * ts.per_xcd;
+        return t < hi ? t : -1;
+    }
+    const int t = b + q * (int)gridDim.x;
+    return t < ts.T ? t : -1;
+}
+
+template <int BK, int NST, int OUT>
+__global__ __attribute__((amdgpu_flat_work_group_size(TT, TT), amdgpu_waves_per_eu(1, 1)))
+void gemm_tile_kernel(GemmArgs g, TileSched ts, int vec_store) {
+    constexpr int ROWB = BK * 2;          // LDS bytes per tile row
+    constexpr int CPR = BK / 8;           // 16-byte chunks per row
+    constexpr int RP = 256 / ROWB;        // rows per 256 bytes
+    constexpr int OPB = TB * ROWB;        // one operand tile
+    constexpr int STAGE = 2 * OPB;        // X tile + W tile
+    constexpr int RPI = 1024 / ROWB;      // rows per 1 KB load instruction
+    constexpr int LPW = OPB / 1024 / 4;   // load instructions per operand per wave
+    constexpr int KS = BK / 16;           // MFMA k-steps per stage
+    static_assert(NST * STAGE <= 160 * 1024, "LDS");
+    __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
+    LDS_PTR(char) lds = (LDS_PTR(char))smem;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
 
-    const char *Abase = (const char *)((const __bf16 *)g.A + (int64_t)shard * g.a_shard + m0 * g.lda);
-    const char *Bbase = (const char *)((const __bf16 *)g.B + (int64_t)shard * g.b_shard + n0 * g.ldb);
-    const int a_rows = (int)min<int64_t>(g.M - m0, TB);
-    const int b_rows = (int)min<int64_t>(g.N - n0, TB);
+    // Number of tiles this workgroup owns.
+    int ntiles = 0;
+    while (tile_of(ts, ntiles) >= 0) ++ntiles;
+    const int nk = (int)(g.K / BK);
+    if (ntiles == 0) return;
+    const int total = ntiles * nk;
 
-    // Per-lane byte offsets of the 8 loads per operand: load j of wave w fills
-    // LDS rows (4j + w)*8 .. +7; lane takes row +lane/8, LDS slot lane%8,
-    // which must hold k-chunk slot ^ (row & 7) = (lane%8) ^ (lane/8).
-    uint32_t aoff[8], boff[8];
-    {
-        const int sub = lane >> 3;
-        const int chunk = (lane & 7) ^ sub;
+    // ---- prefetch cursor (runs NST-1 steps ahead of the compute cursor).
+    // Per-lane load offsets depend on the tile (row clamping), so they are
+    // rebuilt whenever the cursor enters a new tile.
+    int pq = 0, pkt = 0;
+    const char *pa = nullptr, *pb = nullptr;
+    uint32_t aoff[LPW], boff[LPW];
+    auto enter_tile = [&](int q) {
+        int shard, tm, tn;
+        decode_tile(ts, tile_of(ts, q), shard, tm, tn);
+        const int64_t m0 = (int64_t)tm * TB, n0 = (int64_t)tn * TB;
+        pa = (const char *)((const __bf16 *)g.A + (int64_t)shard * g.a_shard + m0 * g.lda);
+        pb = (const char *)((const __bf16 *)g.B + (int64_t)shard * g.b_shard + n0 * g.ldb);
+        const int a_rows = (int)min<int64_t>(g.M - m0, TB);
+        const int b_rows = (int)min<int64_t>(g.N - n0, TB);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int r = (j * 4 + wave) * 8 + sub;
+        for (int j = 0; j < LPW; ++j) {
+            const int r = (j * 4 + wave) * RPI + lane / CPR;
+            const int chunk = (lane % CPR) ^ ((r / RP) % CPR);
             const int ra = r < a_rows ? r : a_rows - 1;
             const int rb = r < b_rows ? r : b_rows - 1;
             aoff[j] = (uint32_t)(((int64_t)ra * g.lda + chunk * 8) * 2);
             boff[j] = (uint32_t)(((int64_t)rb * g.ldb + chunk * 8) * 2);
         }
-    }
-
-    f32x16 acc[4][4];
+    };
+    // Issue loads [j0, j1) of the cursor's step into `stage` (branch-free;
+    // loads 0..LPW-1 fill the X tile, LPW..2*LPW-1 the W tile).
+    auto issue_part = [&](int stage, int j0, int j1) {
+        LDS_PTR(char) dst = lds + stage * STAGE;
+        const int64_t kb = (int64_t)pkt * BK * 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+        for (int j = 0; j < 2 * LPW; ++j) {
+            if (j < j0 || j >= j1) continue;
+            if (j < LPW)
+                __builtin_amdgcn_global_load_lds((const void *)(pa + kb + aoff[j]),
+                                                 (LDS_PTR(void))(dst + (j * 4 + wave) * 1024), 16, 0, 0);
+            else
+                __builtin_amdgcn_global_load_lds(
+                    (const void *)(pb + kb + boff[j - LPW]),
+                    (LDS_PTR(void))(dst + OPB + ((j - LPW) * 4 + wave) * 1024), 16, 0, 0);
+        }
+    };
+    auto issue_step = [&](int stage) { issue_part(stage, 0, 2 * LPW); };
+    // Advance the cursor one step.  Past the last step it stays there, so
+    // later issues reload the last step into stages that are not read again.
+    auto advance = [&]() {
+        if (pq * nk + pkt + 1 < total) {
+            if (++pkt == nk) {
+                pkt = 0;
+                ++pq;
+                enter_tile(pq);
+            }
+        }
+    };
 
-    LDS_PTR(char) lds = (LDS_PTR(char))smem;
-    const int nk = (int)(g.K / TK);
-
-    if (nk > 0) {
-        issue_tile(Abase, aoff, lds, wave);
-        issue_tile(Bbase, boff, lds + OPB, wave);
+    // With two stages the loads of a step are split in halves: the X half is
+    // issued in the last phase of the step two before it (its stage is free
+    // once that step's barrier has passed), the W half in phase 0 of the step
+    // before it.  Spreading them over two phases keeps the vector memory
+    // queue from backing up into the MFMA issue.  With more stages a whole
+    // step is issued in phase 0, NST-1 steps ahead.
+    enter_tile(0);
+    if (NST == 2) {
+        issue_step(0);
+        advance();
+        issue_part(1, 0, LPW);
+    } else {
+#pragma unroll
+        for (int s = 0; s < NST - 1; ++s) {
+            issue_step(s);
+            advance();
+        }
     }
 
     // Fragment addressing: a 32x32x16 operand fragment is 32 rows x 16 k;
-    // lane reads row lane%32, k-chunk 2*ks + lane/32 (8 bf16 = 16 bytes),
-    // stored at slot chunk ^ (row & 7) = chunk ^ (lane & 7).
+    // lane reads row lane%32, k-chunk 2*ks + lane/32.
     const int frow = lane & 31;
     const int fhalf = lane >> 5;
-    const int fx = lane & 7;
-    const int wrow_off = (wn * 128 + frow) * 128;
-    const int xrow_off = (wm * 128 + frow) * 128;
-
-    for (int kt = 0; kt < nk; ++kt) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        LDS_PTR(char) As = lds + (kt & 1) * STAGE;
-        LDS_PTR(char) Bs = As + OPB;
-
-        bf16x8 wf[2][4], xf[2][4];
-        {
-            const int slot = (fhalf ^ fx) << 4;
+    const int fx = (frow / RP) % CPR;
+    const int wrow_off = (wn * 128 + frow) * ROWB;
+    const int xrow_off = (wm * 128 + frow) * ROWB;
+    auto read_frags = [&](bf16x8 (&wd)[4], bf16x8 (&xd)[4], LDS_PTR(char) st, int ks) {
+        const int slot = ((2 * ks + fhalf) ^ fx) << 4;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                wf[0][i] = *(LDS_PTR(bf16x8))(Bs + wrow_off + i * 4096 + slot);
+        for (int i = 0; i < 4; ++i) wd[i] = *(LDS_PTR(bf16x8))(st + OPB + wrow_off + i * 32 * ROWB + slot);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xd[j] = *(LDS_PTR(bf16x8))(st + xrow_off + j * 32 * ROWB + slot);
+    };
+
+    // Step 0's data, then its first fragments.
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPW * (NST - 2)) : "memory");
+    __syncthreads();
+    bf16x8 wf[2][4], xf[2][4];
+    read_frags(wf[0], xf[0], lds, 0);
+
+    // Per K step (KS phases of 16 MFMAs, 8 fragment reads and some
+    // global->LDS loads interleaved one after each MFMA -- one wave per SIMD
+    // issues in order, so memory instructions issued back to back would stall
+    // the wave while its MFMA pipe runs dry):
+    //   phase 0       MFMAs of k-step 0; reads of k-step 1; the loads of the
+    //                 step NST-1 ahead (into the stage freed last step);
+    //   phase ks      MFMAs of k-step ks; reads of k-step ks+1;
+    //   (barrier)     the next step's stage has landed and every wave is done
+    //                 reading this step's stage;
+    //   phase KS-1    MFMAs of the last k-step; reads of the next step's
+    //                 k-step 0, so its LDS latency is hidden too.
+    int it = 0;
+    bool drained = true;  // no epilogue store is in flight
+    for (int q = 0; q < ntiles; ++q) {
+        f32x16 acc[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                xf[0][j] = *(LDS_PTR(bf16x8))(As + xrow_off + j * 4096 + slot);
-        }
-        // Phase ks: issue the fragment reads of step ks+1, then the 16
-        // independent MFMAs of step ks, whose operands were read one phase
-        // earlier.  The fences keep the compiler from mixing phases (which
-        // would put dependent MFMAs back to back).
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            __builtin_amdgcn_sched_barrier(0);
-            const int cur = ks & 1, nx = cur ^ 1;
-            if (ks == 0) {
-                // Prefetch the next K step into the idle stage.  The last
-                // step reloads its own K range there instead, so the body
-                // has no branch; that stage is not read again.
-                const int kn = kt + 1 < nk ? kt + 1 : kt;
-                const int64_t kb = (int64_t)kn * TK * 2;
-                LDS_PTR(char) nxt = lds + ((kt + 1) & 1) * STAGE;
-                issue_tile(Abase + kb, aoff, nxt, wave);
-                issue_tile(Bbase + kb, boff, nxt + OPB, wave);
-            }
-            if (ks < 3) {
-                const int slot = ((2 * (ks + 1) + fhalf) ^ fx) << 4;
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+        for (int kt = 0; kt < nk; ++kt, ++it) {
+            LDS_PTR(char) st = lds + (it % NST) * STAGE;
+            LDS_PTR(char) st_next = lds + ((it + 1) % NST) * STAGE;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    wf[nx][i] = *(LDS_PTR(bf16x8))(Bs + wrow_off + i * 4096 + slot);
+            for (int ks = 0; ks < KS; ++ks) {
+                const int cur = ks & 1, nx = cur ^ 1;
+                if (ks == KS - 1) {
+                    // The next step's loads were issued NST-1 steps ago; the
+                    // NST-2 later groups may stay in flight.  After an epilogue
+                    // its stores are in flight too; then wait for everything.
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (NST == 2 || !drained)
+                        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                    else
+                        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPW * (NST - 2)) : "memory");
+                    drained = true;
+                    __syncthreads();
+                }
+                LDS_PTR(char) rd = ks + 1 < KS ? st : st_next;
+                const int rks = ks + 1 < KS ? ks + 1 : 0;
+                const int slot = ((2 * rks + fhalf) ^ fx) << 4;
+                // Loads of this phase: [j0, j1) of the cursor's step.
+                int j0 = 2 * LPW, j1 = 2 * LPW;
+                if (NST == 2) {
+                    if (ks == 0) { j0 = LPW; j1 = 2 * LPW; }      // W half of step it+1
+                    if (ks == KS - 1) { j0 = 0; j1 = LPW; }       // X half of step it+2
+                } else if (ks == 0) {
+                    j0 = 0; j1 = 2 * LPW;                         // all of step it+NST-1
+                }
+                const int lstage = NST == 2 ? (ks == 0 ? (it + 1) % 2 : it % 2) : (it + NST - 1) % NST;
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    xf[nx][j] = *(LDS_PTR(bf16x8))(As + xrow_off + j * 4096 + slot);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int u = 0; u < 16; ++u) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    // Diagonal order: MFMAs 0..3 touch all 8 fragments, so no
+                    // wait on an LDS read comes after the first global->LDS
+                    // load of the phase (the compiler drains every LDS read at
+                    // such a wait once an LDS-writing load is in flight).
+                    const int i = u & 3, j = ((u & 3) + (u >> 2)) & 3;
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][i], xf[cur][j],
                                                                         acc[i][j], 0, 0, 0);
-            // One MFMA first (it consumes the reads of the previous phase, so
-            // the wait for them never also covers the new ones: at most 8
-            // LDS reads are in flight, within what lgkmcnt can count), then
-            // the next step's 8 reads, then the other 15 MFMAs.  Phase 0
-            // first issues the 16 global->LDS loads of the next K step.
-            if (ks == 0) __builtin_amdgcn_sched_group_barrier(0x020, 16, 0);  // VMEM read
-            if (ks < 3) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // DS read
-                __builtin_amdgcn_sched_group_barrier(0x008, 15, 0);
-            } else {
-                __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    // No global->LDS load may still be writing when the workgroup ends.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-
-    // ---- epilogue.  32x32 D layout with W rows as the row operand:
-    // lane holds m = lane%32 and, for q = 0..3, the 4 columns
-    // n = 8q + 4*(lane/32) + 0..3 in registers 4q..4q+3.
-    const int64_t cbase = (int64_t)shard * g.c_shard;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int64_t m = m0 + wm * 128 + j * 32 + frow;
-        if (m >= g.M) continue;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t n = n0 + wn * 128 + i * 32 + 8 * q + 4 * fhalf;
-                const int64_t o = cbase + m * g.ldc + n;
-                f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                           acc[i][j][4 * q + 3]};
-                if (vec_store && n + 3 < g.N) {
-                    if (OUT == OUT_BF16) {
-                        bf16x4 h = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-                        *(bf16x4 *)((__bf16 *)g.C + o) = h;
-                    } else {
-                        *(f32x4 *)((float *)g.C + o) = v;
+                    if (u < 8) {
+                        if (u < 4)
+                            wf[nx][u] = *(LDS_PTR(bf16x8))(rd + OPB + wrow_off + u * 32 * ROWB + slot);
+                        else
+                            xf[nx][u - 4] = *(LDS_PTR(bf16x8))(rd + xrow_off + (u - 4) * 32 * ROWB + slot);
                     }
-                } else {
+                    // Global->LDS loads in slots 4..15; with more loads than
+                    // slots the first slots take two.
+                    const int n = j1 - j0, extra = n > 12 ? n - 12 : 0;
+                    const int v = u - 4;
+                    const int ls = v < 0 ? 0 : v + (v < extra ? v : extra);
+                    const int lc = v < 0 ? 0 : (v < extra ? 2 : 1);
+                    const int la = j0 + ls < j1 ? j0 + ls : j1;
+                    const int lb = j0 + ls + lc < j1 ? j0 + ls + lc : j1;
+                    if (la < lb) issue_part(lstage, la, lb);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
+                    if (u < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);       // DS read
+                    if (lb - la >= 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // VMEM
+                    if (lb - la >= 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                }
+                if (NST == 2 && ks == 0) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    advance();
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (NST != 2) advance();
+        }
+
+        // ---- epilogue.  32x32 D layout with W rows as the row operand:
+        // lane holds m = lane%32 and, for r4 = 0..3, the 4 columns
+        // n = 8*r4 + 4*(lane/32) + 0..3 in registers 4*r4..4*r4+3.
+        int shard, tm, tn;
+        decode_tile(ts, tile_of(ts, q), shard, tm, tn);
+        const int64_t m0 = (int64_t)tm * TB + wm * 128 + frow;
+        const int64_t n0 = (int64_t)tn * TB + wn * 128 + 4 * fhalf;
+        const int64_t cbase = (int64_t)shard * g.c_shard;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        if (n + e < g.N) {
-                            if (OUT == OUT_BF16) ((__bf16 *)g.C)[o + e] = (__bf16)v[e];
-                            else ((float *)g.C)[o + e] = v[e];
+        for (int j = 0; j < 4; ++j) {
+            const int64_t m = m0 + j * 32;
+            if (m >= g.M) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int64_t n = n0 + i * 32 + 8 * r4;
+                    const int64_t o = cbase + m * g.ldc + n;
+                    const float v0 = acc[i][j][4 * r4], v1 = acc[i][j][4 * r4 + 1];
+                    const float v2 = acc[i][j][4 * r4 + 2], v3 = acc[i][j][4 * r4 + 3];
+                    if (vec_store && n + 3 < g.N) {
+                        if (OUT == OUT_BF16) {
+                            bf16x4 h = {(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
+                            *(bf16x4 *)((__bf16 *)g.C + o) = h;
+                        } else {
+                            *(f32x4 *)((float *)g.C + o) = f32x4{v0, v1, v2, v3};
+                        }
+                    } else {
+                        const float vv[4] = {v0, v1, v2, v3};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            if (n + e < g.N) {
+                                if (OUT == OUT_BF16) ((__bf16 *)g.C)[o + e] = (__bf16)vv[e];
+                                else ((float *)g.C)[o + e] = vv[e];
+                            }
                         }
                     }
                 }
             }
         }
+        drained = false;
     }
+    // No global->LDS load may still be writing when the workgroup ends.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+int num_cus() {
+    static int n = 0;
+    if (n == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            v > 0)
+            n = v;
+        else
+            n = 256;
+    }
+    return n;
+}
+
+// K per stage and number of stages (tuning parameters; 2 x 64 and 4 x 32 both
+// use 128 KB of LDS).
+#ifndef TPL_TILE_BK
+#define TPL_TILE_BK 64
+#endif
+#ifndef TPL_TILE_NST
+#define TPL_TILE_NST 2
+#endif
+constexpr int KERNEL_BK = TPL_TILE_BK;
+constexpr int KERNEL_NST = TPL_TILE_NST;
+
 }  // namespace
 
 bool gemm_tile_supported(const GemmArgs &g) {
-    // 32-bit per-lane offsets: one tile's rows must span < 4 GiB.
+    // 32-bit per-lane offsets: one tile's rows must span < 2 GiB.
     const bool small_rows = (int64_t)TB * (g.lda > g.ldb ? g.lda : g.ldb) * 2 < (1ll << 31);
-    return g.K % TK == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 && g.a_shard % 8 == 0 &&
+    return g.K % KERNEL_BK == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 && g.a_shard % 8 == 0 &&
            g.b_shard % 8 == 0 && aligned16(g.A) && aligned16(g.B) && small_rows;
 }
 
 hipError_t launch_gemm_tile(const GemmArgs &g, int out_type, hipStream_t s) {
     if (g.M == 0 || g.N == 0 || g.P == 0) return hipSuccess;
     const int64_t tm = (g.M + TB - 1) / TB, tn = (g.N + TB - 1) / TB;
-    const int64_t blocks = tm * tn * g.P;
-    if (blocks > 0x7FFFFFFFll) return hipErrorInvalidConfiguration;
+    const int64_t T = tm * tn * g.P;
+    if (T > 0x7FFFFFFFll) return hipErrorInvalidConfiguration;
+    TileSched ts;
+    ts.tiles_m = (int)tm;
+    ts.tiles_n = (int)tn;
+    ts.T = (int)T;
+    const int cus = num_cus();
+    int grid = (int)(T < cus ? T : cus);
+    ts.xcd_split = (grid == cus && cus % 8 == 0 && T >= cus) ? 1 : 0;
+    ts.per_xcd = grid / 8;
     const int esz = out_type == OUT_BF16 ? 2 : 4;
     const int vec = (g.ldc % 4 == 0) && (g.c_shard % 4 == 0) &&
                     (((uintptr_t)g.C) % (uintptr_t)(4 * esz) == 0);
-    dim3 grid((unsigned)blocks), block(TT);
+    dim3 block(TT);
     if (out_type == OUT_BF16)
-        gemm_tile_kernel<OUT_BF16><<<grid, block, 0, s>>>(g, (int)tm, (int)tn, vec);
+        gemm_tile_kernel<KERNEL_BK, KERNEL_NST, OUT_BF16><<<dim3(grid), block, 0, s>>>(g, ts, vec);
     else
-        gemm_tile_kernel<OUT_F32><<<grid, block, 0, s>>>(g, (int)tm, (int)tn, vec);
+        gemm_tile_kernel<KERNEL_BK, KERNEL_NST, OUT_F32><<<dim3(grid), block, 0, s>>>(g, ts, vec);
     return hipGetLastError();
 }
 
