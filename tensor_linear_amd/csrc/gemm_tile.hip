@@ -295,30 +295,47 @@ void gemm_tile_kernel(GemmArgs g, TileSched ts, int vec_store) {
         // n = 8*r4 + 4*(lane/32) + 0..3 in registers 4*r4..4*r4+3.
         int shard, tm, tn;
         decode_tile(ts, tile_of(ts, q), shard, tm, tn);
-        const int64_t m0 = (int64_t)tm * TB + wm * 128 + frow;
-        const int64_t n0 = (int64_t)tn * TB + wn * 128 + 4 * fhalf;
+        const int64_t tm0 = (int64_t)tm * TB, tn0 = (int64_t)tn * TB;
+        const int64_t m0 = tm0 + wm * 128 + frow;
+        const int64_t n0 = tn0 + wn * 128 + 4 * fhalf;
         const int64_t cbase = (int64_t)shard * g.c_shard;
+        constexpr int ESZ = OUT == OUT_BF16 ? 2 : 4;
+        if (vec_store && tm0 + TB <= g.M && tn0 + TB <= g.N) {
+            // Whole tile inside C: one row pointer per 32-row block, every
+            // store at an immediate offset from it.
+            char *base = (char *)g.C + (cbase + m0 * g.ldc + n0) * ESZ;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t m = m0 + j * 32;
-            if (m >= g.M) continue;
+            for (int j = 0; j < 4; ++j) {
+                char *rowp = base + (int64_t)j * 32 * g.ldc * ESZ;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+                for (int i = 0; i < 4; ++i) {
 #pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const int64_t n = n0 + i * 32 + 8 * r4;
-                    const int64_t o = cbase + m * g.ldc + n;
-                    const float v0 = acc[i][j][4 * r4], v1 = acc[i][j][4 * r4 + 1];
-                    const float v2 = acc[i][j][4 * r4 + 2], v3 = acc[i][j][4 * r4 + 3];
-                    if (vec_store && n + 3 < g.N) {
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const f32x4 v = {acc[i][j][4 * r4], acc[i][j][4 * r4 + 1],
+                                         acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]};
+                        char *p = rowp + (i * 32 + 8 * r4) * ESZ;
                         if (OUT == OUT_BF16) {
-                            bf16x4 h = {(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
-                            *(bf16x4 *)((__bf16 *)g.C + o) = h;
+                            const bf16x4 h = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+                            *(bf16x4 *)p = h;
                         } else {
-                            *(f32x4 *)((float *)g.C + o) = f32x4{v0, v1, v2, v3};
+                            *(f32x4 *)p = v;
                         }
-                    } else {
-                        const float vv[4] = {v0, v1, v2, v3};
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t m = m0 + j * 32;
+                if (m >= g.M) continue;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const int64_t n = n0 + i * 32 + 8 * r4;
+                        const int64_t o = cbase + m * g.ldc + n;
+                        const float vv[4] = {acc[i][j][4 * r4], acc[i][j][4 * r4 + 1],
+                                             acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]};
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             if (n + e < g.N) {
