@@ -119,6 +119,25 @@ class Workload:
         self.flops = sum(op[1] for op in self.ops)
 
 
+def traffic_bytes(wid, op):
+    """HBM-side bytes per launch of `op` measured by the rocprofv3 counter
+    passes summarised in profiles/traffic.json, or None when there is no
+    record or the kernel's source has changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))["ops"][str(wid)][op]
+    except (OSError, KeyError, ValueError):
+        return None
+    k = rec["kernel"]
+    base = "tile" if "tile" in k else "skinny" if "skinny" in k else "fold"
+    srcs = {"tile": "gemm_tile.hip", "skinny": "gemm_skinny.hip", "fold": "shard_fold.hip"}[base]
+    h = hashlib.sha256()
+    for f in (srcs, "kernels.h"):
+        h.update(open(os.path.join(ROOT, "tensor_linear_amd", "csrc", f), "rb").read())
+    return rec["bytes"] if h.hexdigest()[:16] == rec["source_sha256_16"] else None
+
+
 def cpu_baseline(wl, rows, np, oracle, torch):
     """Time the oracle on the first `rows` token rows of the workload's GEMMs
     (all output columns), plus the fp32 fold over the same rows."""
@@ -218,11 +237,13 @@ def main():
     d = op_stats[dom]
     if "tflops" in d and wl.wid != 4:
         roof = dict(kernel=dom, bound="mfma", achieved=d["tflops"], peak=PEAK_BF16_TFLOPS,
-                    unit="TFLOP/s", frac=d["tflops"] / PEAK_BF16_TFLOPS, traffic=None,
+                    unit="TFLOP/s", frac=d["tflops"] / PEAK_BF16_TFLOPS,
+                    traffic=traffic_bytes(args.workload, dom),
                     avg_launch_us=d["avg_us"])
     else:
         roof = dict(kernel=dom, bound="hbm", achieved=d["gbps"], peak=PEAK_HBM_GBPS,
-                    unit="GB/s", frac=d["gbps"] / PEAK_HBM_GBPS, traffic=None,
+                    unit="GB/s", frac=d["gbps"] / PEAK_HBM_GBPS,
+                    traffic=traffic_bytes(args.workload, dom),
                     avg_launch_us=d["avg_us"])
 
     out = {
