@@ -86,7 +86,6 @@ class Workload:
             self.Y2 = torch.empty((M, H), dtype=bf, device=dev)
             nbytes = tl.tp_row_workspace_bytes(tl.TP_ROW_FUSED, M, H, P)
             self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-            tl.tp_workspace_zero(self.ws)
             w1b = I * H * 2 + M * H * 2 + M * I * 2
             w2b = H * I * 2 + M * I * 2 + M * H * 2
             self.ops = [

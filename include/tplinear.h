@@ -161,11 +161,12 @@ tp_status tp_linear_column(const void *X, int64_t ldx, const void *W, int64_t ld
  *   (RowParallelLinearWithReplicateOutput; the all-reduce).  The partials are
  *   kept in the workspace.
  * mode TP_ROW_FUSED: the same result, bit for bit, as TP_ROW_SUM.  For
- *   M <= 64 with 16-byte aligned bf16 operands the fold runs in the GEMM's
- *   epilogue: the last workgroup to finish an output tile folds the P
- *   partial tiles.  Other shapes run the TP_ROW_SUM sequence.  The counters
- *   in the workspace must be zero before the first FUSED call on a
- *   workspace (tp_workspace_zero); every call leaves them at zero.
+ *   1 <= M <= 64 with 16-byte aligned bf16 operands the fold runs inside the
+ *   GEMM: each workgroup computes all P shard partials of its output tile
+ *   in ascending order and adds them into a running fp32 sum, so no partial
+ *   reaches memory and the workspace is not touched.  Other shapes run the
+ *   TP_ROW_SUM sequence in the workspace, which is therefore always
+ *   required.
  * mode TP_ROW_SCATTER: requires M % P == 0.  Token slice j = rows
  *   [j*M/P, (j+1)*M/P) of the fold is written to Y + j*y_slice_stride with
  *   row stride ldy (y_slice_stride = 0 means (M/P)*ldy, the contiguous layout
@@ -210,8 +211,8 @@ tp_status tp_shard_reduce(const float *partials, int64_t shard_stride, int64_t l
  * TP_ROW_PARTIAL, and for invalid arguments. */
 size_t tp_row_workspace_bytes(int32_t mode, int64_t M, int64_t N, int32_t P);
 
-/* Queue a fill of `bytes` bytes (a multiple of 4) at `ptr` with zero.  Used
- * to clear a workspace before its first TP_ROW_FUSED call. */
+/* Queue a fill of `bytes` bytes (a multiple of 4) at `ptr` with zero, with a
+ * kernel (no hipMemset node, so it may be captured in a graph). */
 tp_status tp_workspace_zero(void *ptr, size_t bytes, void *stream);
 
 /* A static string naming a status code. */

@@ -3,23 +3,24 @@
 // it streams W from HBM ("模型并行", "Tensor Parallel": Y_i = X W_i for the
 // column form, the partials X_i W_i for the row form).
 //
-// Work unit: one workgroup = one shard i and one 64-column tile of the output
-// (64 rows of W_i), over the shard's whole K range.  Four waves split that K
-// range into four contiguous quarters; each wave loads its W rows and the
-// matching X rows straight from global memory into MFMA fragments
-// (16-byte loads, several k-steps in flight) and multiplies on
-// v_mfma_f32_16x16x32_bf16 with W as the 16-row operand and X as the
-// 16-column operand.  The four wave partials are added through LDS in
-// fixed order (w0 + w1) + w2 + w3.
+// Work unit: one workgroup owns BN = 16 rows of W (16 output columns) and
+// one shard -- or, in the fused row form, all P shards in ascending order.
+// W and X move global -> LDS with global_load_lds_dwordx4 in NST stages of
+// KB columns of K; each 1 KB load instruction covers one contiguous KB*2-byte
+// run of one row, so HBM sees long sequential runs rather than 64-byte
+// pieces of many rows.  In LDS, 16-byte chunk c of row r sits at slot
+// c ^ (r % 16), so the 16 rows of an MFMA fragment read hit 16 different
+// bank groups.  The four waves take four contiguous quarters of each stage's
+// K and multiply on v_mfma_f32_16x16x32_bf16 (W rows as the row operand);
+// their partial sums are added through LDS in the fixed order
+// ((w0 + w1) + w2) + w3 when a shard ends.
 //
-// Fused fold (row form, decode): each workgroup stores its fp32 partial tile,
-// then bumps the tile's counter with an agent-scope release/acquire atomic.
-// The workgroup that sees the count reach P-1 is the last one for that tile:
-// it folds the P partial tiles in ascending shard order, one fp32 add at a
-// time, rounds once, writes Y and puts the counter back to zero.  The order
-// of the adds does not depend on which workgroup arrives last, so the result
-// equals the unfused partial + fold sequence bit for bit.  No workgroup ever
-// waits for another.
+// Fused fold (row form, decode): the shard partials are added into a
+// running fp32 sum in ascending shard order, one add at a time, and the sum
+// is rounded once -- the same operations, in the same order, as writing the
+// partials and running the fold kernel, so the result is bitwise equal to
+// that unfused sequence.  No workspace, counter or cross-workgroup signal is
+// needed.
 #include "kernels.h"
 
 namespace tpl {
@@ -28,9 +29,9 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+#define LDS_PTR(T) __attribute__((address_space(3))) T *
+
 constexpr int SK_THREADS = 256;
-constexpr int SK_WAVES = 4;
-constexpr int SK_NB = SKINNY_BN / 16;  // 16-row W blocks per workgroup
 
 template <int OUT>
 __device__ __forceinline__ void store_out(void *Y, int64_t o, float v) {
@@ -38,174 +39,161 @@ __device__ __forceinline__ void store_out(void *Y, int64_t o, float v) {
     else ((float *)Y)[o] = v;
 }
 
-template <int MB, int U, int OUT, bool FUSED>
+// MB: 16-row blocks of M.  KB: K columns per stage.  NST: stages.
+template <int MB, int KB, int NST, int OUT, bool FOLD>
 __global__ __launch_bounds__(SK_THREADS)
-void gemm_skinny_kernel(GemmArgs g, FoldArgs f, int tiles_n) {
-    __shared__ f32x4 red[SK_WAVES][SK_NB * MB][64];
-
-    const int tn = blockIdx.x / g.P;
-    const int shard = blockIdx.x - tn * g.P;
-    const int64_t n0 = (int64_t)tn * SKINNY_BN;
-
-    const __bf16 *A = (const __bf16 *)g.A + (int64_t)shard * g.a_shard;
-    const __bf16 *B = (const __bf16 *)g.B + (int64_t)shard * g.b_shard;
+void gemm_skinny_kernel(GemmArgs g, FoldArgs f) {
+    constexpr int BN = SKINNY_BN;          // W rows per workgroup
+    constexpr int XR = 16 * MB;            // X rows staged
+    constexpr int ROWB = KB * 2;           // bytes per staged row
+    constexpr int CPR = ROWB / 16;         // 16-byte chunks per row
+    static_assert(CPR >= 16, "rows of at least 256 bytes");
+    constexpr int STB = (BN + XR) * ROWB;  // bytes per stage (rows back to back)
+    constexpr int NI = STB / 1024;         // 1 KB load instructions per stage
+    static_assert(STB % 4096 == 0, "loads split over 4 waves");
+    constexpr int LPW = NI / 4;            // per wave
+    constexpr int SUBS = KB / 32 / 4;      // k32 sub-steps per wave per stage
+    static_assert(SUBS >= 1, "KB >= 128");
+    __shared__ __attribute__((aligned(1024))) char smem[NST * STB];
+    __shared__ f32x4 red[4][MB][64];
+    LDS_PTR(char) lds = (LDS_PTR(char))smem;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int kl = 8 * (lane >> 4);  // this lane's 8-element slice of a k32 step
 
-    // Row pointers; rows past the edge are clamped (their results are never
-    // stored), so every load stays inside the operands.
-    const __bf16 *wrow[SK_NB];
-#pragma unroll
-    for (int nb = 0; nb < SK_NB; ++nb) {
-        int64_t n = n0 + nb * 16 + (lane & 15);
-        if (n > g.N - 1) n = g.N - 1;
-        wrow[nb] = B + n * g.ldb + kl;
+    int tn, s_begin, s_count;
+    if (FOLD) {
+        tn = blockIdx.x; s_begin = 0; s_count = g.P;
+    } else {
+        tn = blockIdx.x / g.P; s_begin = blockIdx.x - tn * g.P; s_count = 1;
     }
-    const __bf16 *xrow[MB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-        int64_t m = mb * 16 + (lane & 15);
-        if (m > g.M - 1) m = g.M - 1;
-        xrow[mb] = A + m * g.lda + kl;
-    }
+    const int64_t n0 = (int64_t)tn * BN;
+    const int64_t Ks = g.K;
+    const int nks = (int)((Ks + KB - 1) / KB);  // stages per shard
+    const int total = s_count * nks;
 
-    f32x4 acc[SK_NB][MB];
+    // ---- load cursor: stage t -> (shard, k stage).  Load instruction q
+    // (= j*4 + wave) fills bytes [q KB, (q+1) KB) of the stage; lane takes
+    // 16-byte unit idx = 64q + lane: row idx / CPR (W rows first, then X
+    // rows), slot idx % CPR, which holds chunk slot ^ (row % 16).
+    int ls = 0, lk = 0;
+    auto issue = [&](int t) {
+        if (t >= total) return;  // uniform
+        const int shard = s_begin + ls;
+        const int64_t kb = (int64_t)lk * KB;
+        LDS_PTR(char) dst = lds + (t % NST) * STB;
 #pragma unroll
-    for (int nb = 0; nb < SK_NB; ++nb)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int64_t nsteps = (g.K + 31) / 32;
-    const int64_t s0 = nsteps * wave / SK_WAVES;
-    const int64_t s1 = nsteps * (wave + 1) / SK_WAVES;
-    const int64_t full = g.K / 32;  // steps with all 32 k inside K
-    const int64_t s_full_end = s1 < full ? s1 : full;
-
-    int64_t s = s0;
-    for (; s + U <= s_full_end; s += U) {
-        bf16x8 wv[U][SK_NB], xv[U][MB];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-#pragma unroll
-            for (int nb = 0; nb < SK_NB; ++nb)
-                wv[u][nb] = __builtin_nontemporal_load((const bf16x8 *)(wrow[nb] + (s + u) * 32));
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-                xv[u][mb] = *(const bf16x8 *)(xrow[mb] + (s + u) * 32);
+        for (int j = 0; j < LPW; ++j) {
+            const int q = j * 4 + wave;
+            const int idx = q * 64 + lane;
+            const int row = idx / CPR, slot = idx % CPR;
+            const int chunk = slot ^ (row & 15);
+            int64_t k = kb + chunk * 8;
+            // K tail: chunks past the shard's K are loaded from column 0 of
+            // the row (in bounds) and zeroed after the fragment read.
+            if (k >= Ks) k = 0;
+            const __bf16 *src;
+            if (row < BN) {
+                int64_t n = n0 + row;
+                if (n > g.N - 1) n = g.N - 1;
+                src = (const __bf16 *)g.B + (int64_t)shard * g.b_shard + n * g.ldb + k;
+            } else {
+                int64_t m = row - BN;
+                if (m > g.M - 1) m = g.M - 1;
+                src = (const __bf16 *)g.A + (int64_t)shard * g.a_shard + m * g.lda + k;
+            }
+            __builtin_amdgcn_global_load_lds((const void *)src,
+                                             (LDS_PTR(void))(dst + q * 1024), 16, 0, 0);
         }
+        if (++lk == nks) { lk = 0; ++ls; }
+    };
+
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+    for (int t = 0; t < NST - 1; ++t) issue(t);
+
+    f32x4 acc[MB];
 #pragma unroll
-            for (int nb = 0; nb < SK_NB; ++nb)
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float run[MB];  // running fused sum, output mapping (see below)
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-                    acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv[u][nb], xv[u][mb],
-                                                                          acc[nb][mb], 0, 0, 0);
-    }
-    for (; s < s1; ++s) {
-        // K % 8 == 0, so a lane's 8-element slice is either all inside K or
-        // all outside; outside slices contribute zero.
-        const bool valid = s * 32 + kl < g.K;
-        bf16x8 wv[SK_NB], xv[MB];
+    for (int mb = 0; mb < MB; ++mb) run[mb] = 0.f;
+
+    const int frow = lane & 15;   // fragment row
+    const int fk = lane >> 4;     // fragment 8-column group
+    int cs = 0, ck = 0;           // compute cursor (shard index, k stage)
+    for (int t = 0; t < total; ++t) {
+        // Stage t's loads were issued NST-1 stages ago; NST-2 later stages'
+        // loads may stay in flight.
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW * (NST - 2)) : "memory");
+        __syncthreads();
+        issue(t + NST - 1);
+        LDS_PTR(char) st = lds + (t % NST) * STB;
+        const int64_t kb = (int64_t)ck * KB;
 #pragma unroll
-        for (int nb = 0; nb < SK_NB; ++nb) {
-            wv[nb] = bf16x8{};
-            if (valid) wv[nb] = *(const bf16x8 *)(wrow[nb] + s * 32);
+        for (int sub = 0; sub < SUBS; ++sub) {
+            const int c = (wave * SUBS + sub) * 4 + fk;  // chunk within the stage
+            const bool valid = kb + c * 8 < Ks;
+            bf16x8 wv = *(LDS_PTR(bf16x8))(st + frow * ROWB + ((c ^ frow) << 4));
+            if (!valid) wv = bf16x8{};
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const int xr = BN + mb * 16 + frow;
+                bf16x8 xv = *(LDS_PTR(bf16x8))(st + xr * ROWB + ((c ^ (xr & 15)) << 4));
+                if (!valid) xv = bf16x8{};
+                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv, xv, acc[mb], 0, 0, 0);
+            }
         }
+        if (++ck < nks) continue;
+
+        // ---- shard finished: add the four waves' partials in fixed order.
+        // Output (n, m) of the tile sits in lane 16*(n/4) + m%16, register
+        // n%4, block m/16 (16x16 D layout, W rows as the row operand).
+        // Thread tid takes n = tid % 16, m = tid / 16 + 16*mb.
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-            xv[mb] = bf16x8{};
-            if (valid) xv[mb] = *(const bf16x8 *)(xrow[mb] + s * 32);
+            red[wave][mb][lane] = acc[mb];
+            acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        __syncthreads();
+        const int on = tid & 15, om = tid >> 4;
+        const int src_lane = 16 * (on >> 2) + om, src_r = on & 3;
+        const int shard = s_begin + cs;
 #pragma unroll
-        for (int nb = 0; nb < SK_NB; ++nb)
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-                acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv[nb], xv[mb], acc[nb][mb], 0, 0, 0);
-    }
-
-#pragma unroll
-    for (int nb = 0; nb < SK_NB; ++nb)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) red[wave][nb * MB + mb][lane] = acc[nb][mb];
-    __syncthreads();
-
-    // Output element (m, n) of the tile sits in block (n/16, m/16) at lane
-    // 16*((n%16)/4) + m%16, register n%4 (16x16 MFMA D layout with W rows as
-    // the row operand).  Threads take consecutive n for coalesced stores.
-    constexpr int OUTS = 64 * 16 * MB / SK_THREADS;
-    float val[OUTS];
-    int64_t mm[OUTS], nn[OUTS];
-#pragma unroll
-    for (int e = 0; e < OUTS; ++e) {
-        const int idx = tid + e * SK_THREADS;
-        const int n = idx & 63, m = idx >> 6;
-        const int blk = (n >> 4) * MB + (m >> 4);
-        const int ln = 16 * ((n & 15) >> 2) + (m & 15);
-        const int r = n & 3;
-        float v = red[0][blk][ln][r];
-        v = v + red[1][blk][ln][r];
-        v = v + red[2][blk][ln][r];
-        v = v + red[3][blk][ln][r];
-        val[e] = v;
-        mm[e] = m;
-        nn[e] = n0 + n;
-    }
-
-    if (!FUSED) {
-#pragma unroll
-        for (int e = 0; e < OUTS; ++e)
-            if (mm[e] < g.M && nn[e] < g.N)
-                store_out<OUT>(g.C, (int64_t)shard * g.c_shard + mm[e] * g.ldc + nn[e], val[e]);
-        return;
-    }
-
-    // Fused: publish this shard's partial tile, then count arrivals.
-    const int64_t part_stride = g.M * g.N;
-#pragma unroll
-    for (int e = 0; e < OUTS; ++e)
-        if (mm[e] < g.M && nn[e] < g.N)
-            f.partials[(int64_t)shard * part_stride + mm[e] * g.N + nn[e]] = val[e];
-    __threadfence();
-    __syncthreads();
-    __shared__ uint32_t s_last;
-    if (tid == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(&f.counters[tn], 1u, __ATOMIC_ACQ_REL,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (old == (uint32_t)(g.P - 1)) ? 1u : 0u;
-    }
-    __syncthreads();
-    if (s_last == 0u) return;
-    __threadfence();
-#pragma unroll
-    for (int e = 0; e < OUTS; ++e) {
-        if (mm[e] < g.M && nn[e] < g.N) {
-            const float *p = f.partials + mm[e] * g.N + nn[e];
-            float a = __builtin_nontemporal_load(p);
-            for (int i = 1; i < g.P; ++i) a = a + __builtin_nontemporal_load(p + (int64_t)i * part_stride);
-            store_out<OUT>(f.Y, mm[e] * f.ldy + nn[e], a);
+        for (int mb = 0; mb < MB; ++mb) {
+            float v = red[0][mb][src_lane][src_r];
+            v = v + red[1][mb][src_lane][src_r];
+            v = v + red[2][mb][src_lane][src_r];
+            v = v + red[3][mb][src_lane][src_r];
+            const int64_t m = om + 16 * mb, n = n0 + on;
+            if (FOLD) {
+                run[mb] = cs == 0 ? v : run[mb] + v;
+                if (cs == s_count - 1 && m < g.M && n < g.N)
+                    store_out<OUT>(f.Y, m * f.ldy + n, run[mb]);
+            } else if (m < g.M && n < g.N) {
+                store_out<OUT>(g.C, (int64_t)shard * g.c_shard + m * g.ldc + n, v);
+            }
         }
+        ck = 0;
+        ++cs;
+        // `red` is written again only after at least one more barrier.
     }
-    if (tid == 0)
-        __hip_atomic_store(&f.counters[tn], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <int MB, int U>
+template <int MB, int KB, int NST>
 hipError_t launch_mb(const GemmArgs &g, int out_type, const FoldArgs *fold, hipStream_t s) {
     const int64_t tn = (g.N + SKINNY_BN - 1) / SKINNY_BN;
-    const int64_t blocks = tn * g.P;
+    const int64_t blocks = fold ? tn : tn * g.P;
     if (blocks > 0x7FFFFFFFll) return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)blocks), block(SK_THREADS);
-    FoldArgs f = fold ? *fold : FoldArgs{nullptr, 0, 0, nullptr, nullptr};
+    FoldArgs f = fold ? *fold : FoldArgs{nullptr, 0, 0};
     if (fold) {
-        if (out_type == OUT_BF16) gemm_skinny_kernel<MB, U, OUT_BF16, true><<<grid, block, 0, s>>>(g, f, (int)tn);
-        else gemm_skinny_kernel<MB, U, OUT_F32, true><<<grid, block, 0, s>>>(g, f, (int)tn);
+        if (out_type == OUT_BF16) gemm_skinny_kernel<MB, KB, NST, OUT_BF16, true><<<grid, block, 0, s>>>(g, f);
+        else gemm_skinny_kernel<MB, KB, NST, OUT_F32, true><<<grid, block, 0, s>>>(g, f);
     } else {
-        if (out_type == OUT_BF16) gemm_skinny_kernel<MB, U, OUT_BF16, false><<<grid, block, 0, s>>>(g, f, (int)tn);
-        else gemm_skinny_kernel<MB, U, OUT_F32, false><<<grid, block, 0, s>>>(g, f, (int)tn);
+        if (out_type == OUT_BF16) gemm_skinny_kernel<MB, KB, NST, OUT_BF16, false><<<grid, block, 0, s>>>(g, f);
+        else gemm_skinny_kernel<MB, KB, NST, OUT_F32, false><<<grid, block, 0, s>>>(g, f);
     }
     return hipGetLastError();
 }
@@ -215,7 +203,7 @@ inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 }  // namespace
 
 bool gemm_skinny_supported(const GemmArgs &g) {
-    return g.M >= 1 && g.M <= SKINNY_MAX_M && g.K % 8 == 0 && g.lda % 8 == 0 &&
+    return g.M >= 1 && g.M <= SKINNY_MAX_M && g.K > 0 && g.K % 8 == 0 && g.lda % 8 == 0 &&
            g.ldb % 8 == 0 && g.a_shard % 8 == 0 && g.b_shard % 8 == 0 &&
            aligned16(g.A) && aligned16(g.B);
 }
@@ -223,9 +211,17 @@ bool gemm_skinny_supported(const GemmArgs &g) {
 hipError_t launch_gemm_skinny(const GemmArgs &g, int out_type, const FoldArgs *fold,
                               hipStream_t s) {
     if (g.M == 0 || g.N == 0 || g.P == 0) return hipSuccess;
-    if (g.M <= 16) return launch_mb<1, 4>(g, out_type, fold, s);
-    if (g.M <= 32) return launch_mb<2, 4>(g, out_type, fold, s);
-    return launch_mb<4, 2>(g, out_type, fold, s);
+    // LDS per workgroup: NST * (16 + 16*MB) * KB * 2 bytes, plus the
+    // cross-wave sums.  Two stages; small stages let several workgroups share
+    // a CU, which keeps more loads in flight when the grid is large (one
+    // workgroup per 16 output columns and shard); the fused fold has a P
+    // times smaller grid and streams better with larger stages.
+    if (g.M <= 16) {
+        if (fold) return launch_mb<1, 512, 2>(g, out_type, fold, s);   // 64 KB
+        return launch_mb<1, 256, 2>(g, out_type, fold, s);             // 32 KB
+    }
+    if (g.M <= 32) return launch_mb<2, 256, 2>(g, out_type, fold, s);  // 48 KB
+    return launch_mb<4, 256, 2>(g, out_type, fold, s);                 // 80 KB
 }
 
 }  // namespace tpl

@@ -24,13 +24,11 @@ struct GemmArgs {
 enum InType { IN_F32 = 0, IN_BF16 = 1 };
 enum OutType { OUT_F32 = 0, OUT_BF16 = 1 };
 
-// Fused fold for the skinny row GEMM: the last workgroup to finish an
-// output tile folds the P partial tiles (stored in `partials`, part i at
-// partials + i*M*N, row stride N) into Y.
+// Fused fold for the skinny row GEMM: each workgroup walks all P shards of
+// its output tile in ascending order and adds the shard partials into a
+// running fp32 sum, written once to Y.
 struct FoldArgs {
     void *Y; int64_t ldy; int32_t out_type;
-    float *partials;
-    uint32_t *counters;  // one per N tile, zero on entry, zero on exit
 };
 
 // 256x256x64 bf16 MFMA tile kernel.  Requires K % 64 == 0, lda, ldb,
@@ -38,15 +36,15 @@ struct FoldArgs {
 hipError_t launch_gemm_tile(const GemmArgs &g, int out_type, hipStream_t s);
 bool gemm_tile_supported(const GemmArgs &g);
 
-// Skinny (M <= 64) bf16 kernel that streams W.  Requires K % 8 == 0,
+// Skinny (M <= 64) bf16 kernel that streams W.  Requires K > 0, K % 8 == 0,
 // lda, ldb, a_shard, b_shard multiples of 8 and A, B 16-byte aligned.
-// fold == nullptr: C_i written as out_type.  fold != nullptr: C is unused;
-// the partials go to fold->partials and the fold writes fold->Y.
+// fold == nullptr: C_i written as out_type.  fold != nullptr: C is unused
+// and the fold of the P shard products is written to fold->Y.
 hipError_t launch_gemm_skinny(const GemmArgs &g, int out_type, const FoldArgs *fold,
                               hipStream_t s);
 bool gemm_skinny_supported(const GemmArgs &g);
 constexpr int SKINNY_MAX_M = 64;
-constexpr int SKINNY_BN = 64;
+constexpr int SKINNY_BN = 16;
 
 // Any shape, stride or alignment; fp32 or bf16 inputs.
 hipError_t launch_gemm_generic(const GemmArgs &g, int in_type, int out_type, hipStream_t s);

@@ -45,11 +45,6 @@ size_t partials_bytes(int64_t M, int64_t N, int32_t P) {
     return round_up((size_t)P * (size_t)M * (size_t)N * sizeof(float), WS_ALIGN);
 }
 
-size_t counters_bytes(int64_t N) {
-    const size_t tiles = (size_t)((N + SKINNY_BN - 1) / SKINNY_BN);
-    return round_up(tiles * sizeof(uint32_t), WS_ALIGN);
-}
-
 }  // namespace
 
 extern "C" {
@@ -134,8 +129,8 @@ size_t tp_row_workspace_bytes(int32_t mode, int64_t M, int64_t N, int32_t P) {
     if (M < 0 || N < 0 || P < 1 || P > TP_MAX_SHARDS) return 0;
     switch (mode) {
         case TP_ROW_SUM:
+        case TP_ROW_FUSED:
         case TP_ROW_SCATTER: return partials_bytes(M, N, P);
-        case TP_ROW_FUSED: return partials_bytes(M, N, P) + counters_bytes(N);
         default: return 0;
     }
 }
@@ -177,8 +172,6 @@ tp_status tp_linear_row(const void *X, int64_t ldx, const void *W, int64_t ldw, 
     if (mode == TP_ROW_FUSED && dtype == TP_BF16 && gemm_skinny_supported(g)) {
         FoldArgs f;
         f.Y = Y; f.ldy = ldy; f.out_type = out;
-        f.partials = parts;
-        f.counters = (uint32_t *)((char *)workspace + partials_bytes(M, N, P));
         return hip_status(launch_gemm_skinny(g, out, &f, s));
     }
 

@@ -160,12 +160,12 @@ def test_row_errors():
     assert row(ws=None) == tl.TP_ERR_WORKSPACE
     assert row(wsb=need - 1) == tl.TP_ERR_WORKSPACE
     assert row(ws=FWS + 4) == tl.TP_ERR_WORKSPACE              # not 256-byte aligned
-    assert row(mode=tl.TP_ROW_FUSED, wsb=need) == tl.TP_ERR_WORKSPACE  # + counters
+    assert row(mode=tl.TP_ROW_FUSED, wsb=need - 1) == tl.TP_ERR_WORKSPACE
     assert row(M=0) == tl.TP_OK
     assert tl.tp_row_workspace_bytes(tl.TP_ROW_PARTIAL, 4, 12, 4) == 0
     assert tl.tp_row_workspace_bytes(tl.TP_ROW_SUM, 4, 12, 0) == 0
     fused = tl.tp_row_workspace_bytes(tl.TP_ROW_FUSED, 16, 8192, 8)
-    assert fused >= 8 * 16 * 8192 * 4 + (8192 // 64) * 4
+    assert fused == tl.tp_row_workspace_bytes(tl.TP_ROW_SUM, 16, 8192, 8) >= 8 * 16 * 8192 * 4
 
 
 def test_reduce_errors():
