@@ -89,8 +89,10 @@ void gemm_tile_kernel(GemmArgs g, TileSched ts, int vec_store) {
     constexpr int RPI = 1024 / ROWB;      // rows per 1 KB load instruction
     constexpr int LPW = OPB / 1024 / 4;   // load instructions per operand per wave
     constexpr int KS = BK / 16;           // MFMA k-steps per stage
-    static_assert(NST * STAGE <= 160 * 1024, "LDS");
-    __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
+    constexpr int EPI_ROWB = 32 * 4 + 16;   // one fp32 row of a 32x32 block, padded
+    constexpr int EPI_WAVE = 32 * EPI_ROWB; // per-wave staging area
+    static_assert(NST * STAGE + 4 * EPI_WAVE <= 160 * 1024, "LDS");
+    __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE + 4 * EPI_WAVE];
     LDS_PTR(char) lds = (LDS_PTR(char))smem;
 
     const int tid = threadIdx.x;
@@ -296,51 +298,58 @@ void gemm_tile_kernel(GemmArgs g, TileSched ts, int vec_store) {
         int shard, tm, tn;
         decode_tile(ts, tile_of(ts, q), shard, tm, tn);
         const int64_t tm0 = (int64_t)tm * TB, tn0 = (int64_t)tn * TB;
-        const int64_t m0 = tm0 + wm * 128 + frow;
-        const int64_t n0 = tn0 + wn * 128 + 4 * fhalf;
         const int64_t cbase = (int64_t)shard * g.c_shard;
-        constexpr int ESZ = OUT == OUT_BF16 ? 2 : 4;
-        if (vec_store && tm0 + TB <= g.M && tn0 + TB <= g.N) {
-            // Whole tile inside C: one row pointer per 32-row block, every
-            // store at an immediate offset from it.
-            char *base = (char *)g.C + (cbase + m0 * g.ldc + n0) * ESZ;
+        // Each 32x32 block goes through this wave's LDS area: written in its
+        // MFMA layout (lane: row m, four consecutive n), read back
+        // row-contiguous, so a store covers whole 64-byte (bf16) or 128-byte
+        // (fp32) row segments.  One path for all tiles: only stores that
+        // cross M or N fall back to element stores.
+        {
+            LDS_PTR(char) ep = lds + NST * STAGE + wave * EPI_WAVE;
+            const int64_t tm_w = tm0 + wm * 128, tn_w = tn0 + wn * 128;
+            constexpr int VW = OUT == OUT_BF16 ? 8 : 4;   // values per lane store
+            constexpr int RPP = 64 * VW / 32;              // rows per pass
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                char *rowp = base + (int64_t)j * 32 * g.ldc * ESZ;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int r4 = 0; r4 < 4; ++r4) {
                         const f32x4 v = {acc[i][j][4 * r4], acc[i][j][4 * r4 + 1],
                                          acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]};
-                        char *p = rowp + (i * 32 + 8 * r4) * ESZ;
-                        if (OUT == OUT_BF16) {
-                            const bf16x4 h = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-                            *(bf16x4 *)p = h;
-                        } else {
-                            *(f32x4 *)p = v;
-                        }
+                        *(LDS_PTR(f32x4))(ep + frow * EPI_ROWB + (8 * r4 + 4 * fhalf) * 4) = v;
                     }
-                }
-            }
-        } else {
+                    const int64_t bm = tm_w + j * 32, bn = tn_w + i * 32;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t m = m0 + j * 32;
-                if (m >= g.M) continue;
+                    for (int pp = 0; pp < 32 / RPP; ++pp) {
+                        const int r = pp * RPP + lane / (32 / VW), c = VW * (lane % (32 / VW));
+                        const int64_t m = bm + r, n = bn + c;
+                        float vv[VW];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                        for (int h = 0; h < VW / 4; ++h) {
+                            const f32x4 a4 = *(LDS_PTR(f32x4))(ep + r * EPI_ROWB + (c + 4 * h) * 4);
+                            vv[4 * h] = a4[0]; vv[4 * h + 1] = a4[1]; vv[4 * h + 2] = a4[2]; vv[4 * h + 3] = a4[3];
+                        }
+                        if (m < g.M) {
+                            const int64_t o = cbase + m * g.ldc + n;
+                            if (vec_store && n + VW <= g.N) {
+                                if (OUT == OUT_BF16) {
+                                    bf16x8 hv;
 #pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) {
-                        const int64_t n = n0 + i * 32 + 8 * r4;
-                        const int64_t o = cbase + m * g.ldc + n;
-                        const float vv[4] = {acc[i][j][4 * r4], acc[i][j][4 * r4 + 1],
-                                             acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]};
+                                    for (int e = 0; e < 8; ++e) hv[e] = (__bf16)vv[e];
+                                    *(bf16x8 *)((__bf16 *)g.C + o) = hv;
+                                } else {
+                                    *(f32x4 *)((float *)g.C + o) = f32x4{vv[0], vv[1], vv[2], vv[3]};
+                                }
+                            } else {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            if (n + e < g.N) {
-                                if (OUT == OUT_BF16) ((__bf16 *)g.C)[o + e] = (__bf16)vv[e];
-                                else ((float *)g.C)[o + e] = vv[e];
+                                for (int e = 0; e < VW; ++e) {
+                                    if (n + e < g.N) {
+                                        if (OUT == OUT_BF16) ((__bf16 *)g.C)[o + e] = (__bf16)vv[e];
+                                        else ((float *)g.C)[o + e] = vv[e];
+                                    }
+                                }
                             }
                         }
                     }
@@ -402,9 +411,10 @@ hipError_t launch_gemm_tile(const GemmArgs &g, int out_type, hipStream_t s) {
     int grid = (int)(T < cus ? T : cus);
     ts.xcd_split = (grid == cus && cus % 8 == 0 && T >= cus) ? 1 : 0;
     ts.per_xcd = grid / 8;
-    const int esz = out_type == OUT_BF16 ? 2 : 4;
-    const int vec = (g.ldc % 4 == 0) && (g.c_shard % 4 == 0) &&
-                    (((uintptr_t)g.C) % (uintptr_t)(4 * esz) == 0);
+    // 16-byte stores of 8 bf16 or 4 fp32 values: row starts and shard offsets
+    // must keep that alignment.
+    const int vw = out_type == OUT_BF16 ? 8 : 4;
+    const int vec = (g.ldc % vw == 0) && (g.c_shard % vw == 0) && (((uintptr_t)g.C) % 16 == 0);
     dim3 block(TT);
     if (out_type == OUT_BF16)
         gemm_tile_kernel<KERNEL_BK, KERNEL_NST, OUT_BF16><<<dim3(grid), block, 0, s>>>(g, ts, vec);
