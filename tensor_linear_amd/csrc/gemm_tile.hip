@@ -303,7 +303,10 @@ void gemm_tile_kernel(GemmArgs g, TileSched ts, int vec_store) {
         // MFMA layout (lane: row m, four consecutive n), read back
         // row-contiguous, so a store covers whole 64-byte (bf16) or 128-byte
         // (fp32) row segments.  One path for all tiles: only stores that
-        // cross M or N fall back to element stores.
+        // cross M or N fall back to element stores.  The stores are
+        // non-temporal: every CU reaches its epilogue at about the same time,
+        // and streaming the burst past L2 keeps it from filling the L2 with
+        // dirty lines the next loads would have to wait behind.
         {
             LDS_PTR(char) ep = lds + NST * STAGE + wave * EPI_WAVE;
             const int64_t tm_w = tm0 + wm * 128, tn_w = tn0 + wn * 128;
@@ -338,9 +341,10 @@ void gemm_tile_kernel(GemmArgs g, TileSched ts, int vec_store) {
                                     bf16x8 hv;
 #pragma unroll
                                     for (int e = 0; e < 8; ++e) hv[e] = (__bf16)vv[e];
-                                    *(bf16x8 *)((__bf16 *)g.C + o) = hv;
+                                    __builtin_nontemporal_store(hv, (bf16x8 *)((__bf16 *)g.C + o));
                                 } else {
-                                    *(f32x4 *)((float *)g.C + o) = f32x4{vv[0], vv[1], vv[2], vv[3]};
+                                    __builtin_nontemporal_store(f32x4{vv[0], vv[1], vv[2], vv[3]},
+                                                                (f32x4 *)((float *)g.C + o));
                                 }
                             } else {
 #pragma unroll
