@@ -134,7 +134,10 @@ def _mat(t, name):
         raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
     if t.shape[1] > 1 and t.stride(1) != 1:
         raise ValueError(f"{name} must have unit column stride")
-    ld = t.stride(0) if t.shape[0] > 1 else max(t.shape[1], 1)
+    # A one-row view keeps the row stride of the buffer it was cut from when
+    # that stride is a valid leading dim (it places the blocks of a [P, 1, N]
+    # output); otherwise its leading dim is its width.
+    ld = t.stride(0) if t.shape[0] > 1 or t.stride(0) >= t.shape[1] else t.shape[1]
     return t.data_ptr(), t.shape[0], t.shape[1], max(ld, t.shape[1], 1)
 
 

@@ -10,10 +10,13 @@
 // run of one row, so HBM sees long sequential runs rather than 64-byte
 // pieces of many rows.  In LDS, 16-byte chunk c of row r sits at slot
 // c ^ (r % 16), so the 16 rows of an MFMA fragment read hit 16 different
-// bank groups.  The four waves take four contiguous quarters of each stage's
-// K and multiply on v_mfma_f32_16x16x32_bf16 (W rows as the row operand);
-// their partial sums are added through LDS in the fixed order
-// ((w0 + w1) + w2) + w3 when a shard ends.
+// bank groups.  The shard's K is cut into 32-column blocks; wave w takes the
+// blocks whose index is w mod 4, in ascending order, and multiplies on
+// v_mfma_f32_16x16x32_bf16 (W rows as the row operand).  The four wave sums
+// are added through LDS in the fixed order ((w0 + w1) + w2) + w3 when a
+// shard ends.  Since a stage holds a multiple of four blocks, which blocks
+// each wave adds, and in which order, does not depend on the stage size:
+// every instantiation gives the same fp32 result for the same shard.
 //
 // Fused fold (row form, decode): the shard partials are added into a
 // running fp32 sum in ascending shard order, one add at a time, and the sum
@@ -132,7 +135,7 @@ void gemm_skinny_kernel(GemmArgs g, FoldArgs f) {
         const int64_t kb = (int64_t)ck * KB;
 #pragma unroll
         for (int sub = 0; sub < SUBS; ++sub) {
-            const int c = (wave * SUBS + sub) * 4 + fk;  // chunk within the stage
+            const int c = (sub * 4 + wave) * 4 + fk;  // chunk within the stage
             const bool valid = kb + c * 8 < Ks;
             bf16x8 wv = *(LDS_PTR(bf16x8))(st + frow * ROWB + ((c ^ frow) << 4));
             if (!valid) wv = bf16x8{};

@@ -25,7 +25,7 @@
 // different 16-byte bank groups.
 //
 // Edges: rows past M or N are clamped to the last valid row (their results
-// are not stored).  K must be a multiple of BK.
+// are not stored).  K must be a positive multiple of BK.
 #include "kernels.h"
 
 namespace tpl {
@@ -398,7 +398,7 @@ constexpr int KERNEL_NST = TPL_TILE_NST;
 bool gemm_tile_supported(const GemmArgs &g) {
     // 32-bit per-lane offsets: one tile's rows must span < 2 GiB.
     const bool small_rows = (int64_t)TB * (g.lda > g.ldb ? g.lda : g.ldb) * 2 < (1ll << 31);
-    return g.K % KERNEL_BK == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 && g.a_shard % 8 == 0 &&
+    return g.K > 0 && g.K % KERNEL_BK == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 && g.a_shard % 8 == 0 &&
            g.b_shard % 8 == 0 && aligned16(g.A) && aligned16(g.B) && small_rows;
 }
 

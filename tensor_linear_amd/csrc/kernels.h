@@ -31,7 +31,7 @@ struct FoldArgs {
     void *Y; int64_t ldy; int32_t out_type;
 };
 
-// 256x256x64 bf16 MFMA tile kernel.  Requires K % 64 == 0, lda, ldb,
+// 256x256x64 bf16 MFMA tile kernel.  Requires K > 0, K % 64 == 0, lda, ldb,
 // a_shard, b_shard multiples of 8 and A, B 16-byte aligned.
 hipError_t launch_gemm_tile(const GemmArgs &g, int out_type, hipStream_t s);
 bool gemm_tile_supported(const GemmArgs &g);

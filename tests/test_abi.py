@@ -185,3 +185,16 @@ def test_workspace_zero_errors():
     assert tl.lib.tp_workspace_zero(None, 16, None) == tl.TP_ERR_NULL
     assert tl.lib.tp_workspace_zero(FWS, 6, None) == tl.TP_ERR_SHAPE
     assert tl.lib.tp_workspace_zero(None, 0, None) == tl.TP_OK
+
+
+def test_binding_leading_dims():
+    """The binding's (rows, cols, leading dim) of 2-D views, host only."""
+    import torch
+    buf = torch.zeros(4 * 1 * 40)
+    parts = buf.view(4, 1, 40)[:, :, 3:19]          # [P, 1, N] cut from rows of 40
+    assert tl._mat(parts[0], "Y")[1:] == (1, 16, 40)
+    assert tl._mat(torch.zeros(1, 16), "Y")[1:] == (1, 16, 16)
+    assert tl._mat(torch.zeros(5, 16)[:, :8], "Y")[1:] == (5, 8, 16)
+    assert tl._mat(torch.zeros(0, 5), "Y")[1:] == (0, 5, 5)
+    with pytest.raises(ValueError):
+        tl._mat(torch.zeros(4, 6).t(), "Y")
