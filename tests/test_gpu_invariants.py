@@ -14,7 +14,8 @@ and an accumulation-order difference would show:
     the decode shapes it fuses;
   * TP_ROW_SCATTER slices are the row blocks of TP_ROW_SUM, with and without
     gaps between the slices;
-  * nothing outside an output view is written (guard cells keep their bits).
+  * nothing outside an output view is written (guard cells keep their bits);
+  * K = 0 gives +0 everywhere (an empty sum), in every mode.
 """
 import numpy as np
 import pytest
@@ -222,3 +223,19 @@ def test_guard_cells(shape, col0):
     tl.tp_linear_row(X, W, Yp, P, tl.TP_ROW_PARTIAL)
     assert _guard_ok(buf, mask_of(buf.numel(), off, P * M)), "partials wrote outside"
     assert not torch.isnan(Yp).any()
+
+
+@pytest.mark.parametrize("M,N,P", [(300, 512, 8), (16, 1000, 8), (5, 24, 3)])
+def test_zero_k(M, N, P):
+    """K = 0: an empty sum, so every output is +0 (and nothing is read)."""
+    for dt in ("bf16", "f32"):
+        tdt = _tdt(dt)
+        X = torch.empty((M, 0), dtype=tdt, device=DEV)
+        W = torch.empty((N, 0), dtype=tdt, device=DEV)
+        Y = torch.full((M, N), 7.0, dtype=tdt, device=DEV)
+        tl.tp_linear_column(X, W, Y, P)
+        assert not bits(Y).any(), "column"
+        for mode in (tl.TP_ROW_SUM, tl.TP_ROW_FUSED):
+            Y.fill_(7.0)
+            tl.tp_linear_row(X, W, Y, P, mode, workspace(mode, M, N, P))
+            assert not bits(Y).any(), f"row mode {mode}"
