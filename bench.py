@@ -12,7 +12,8 @@ same kernels TP_ROW_SUM runs, called separately so each is timed).
 Prints ONE JSON line.  `value` is the step's GEMM TFLOP/s; `roofline` is for
 the dominant kernel (the fc1 column GEMM, MFMA-bound), its time measured with
 HIP events on the stream it runs on; `cpu_baseline` times the CPU oracle on a
-bounded sample of the same workload.
+bounded sample of the same workload; `context` holds figures taken outside the
+timed step (each GEMM's shard 0 alone at its real shape, a plain device copy).
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload 2|3|4|5]
 """
@@ -116,6 +117,45 @@ class Workload:
                         "reduce-scatter over tokens, all-gather view -> column 8192->28672"
             self.shape = dict(M=M, K=K, N=N, N_next=N3, P=P)
         self.flops = sum(op[1] for op in self.ops)
+        self.single = self._single_shard_ops(P, torch, tl)
+
+    def _single_shard_ops(self, P, torch, tl):
+        """Shard 0 of each GEMM alone, at its real shape (one GPU's share of
+        the layer): (name, flop, bytes, fn).  Timed outside the step."""
+        dev, bf = "cuda:0", torch.bfloat16
+        ops = []
+        def col(name, X, W):
+            Ns = W.shape[0] // P
+            Y = torch.empty((X.shape[0], Ns), dtype=bf, device=dev)
+            Wi = W[:Ns]
+            fl = 2.0 * X.shape[0] * Ns * X.shape[1]
+            nb = (Wi.numel() + X.numel() + Y.numel()) * 2
+            ops.append((name, fl, nb, lambda: tl.tp_linear_column(X, Wi, Y, 1)))
+        def row(name, X, W, fused):
+            Ks = X.shape[1] // P
+            Xi, Wi = X[:, :Ks], W[:, :Ks]
+            M, N = X.shape[0], W.shape[0]
+            fl = 2.0 * M * N * Ks
+            if fused:
+                Y = torch.empty((M, N), dtype=bf, device=dev)
+                ws = torch.empty(tl.tp_row_workspace_bytes(tl.TP_ROW_FUSED, M, N, 1),
+                                 dtype=torch.uint8, device=dev)
+                nb = (Wi.numel() + Xi.numel() + Y.numel()) * 2
+                ops.append((name, fl, nb, lambda: tl.tp_linear_row(Xi, Wi, Y, 1, tl.TP_ROW_FUSED, ws)))
+            else:
+                part = torch.empty((1, M, N), dtype=torch.float32, device=dev)
+                nb = (Wi.numel() + Xi.numel()) * 2 + part.numel() * 4
+                ops.append((name, fl, nb, lambda: tl.tp_linear_row(Xi, Wi, part, 1, tl.TP_ROW_PARTIAL)))
+        if self.wid in (2, 3):
+            col("column_gemm_one_shard", self.X1, self.W1)
+            row("row_gemm_one_shard", self.X2, self.W2, False)
+        elif self.wid == 4:
+            col("column_gemm_decode_one_shard", self.X1, self.W1)
+            row("row_gemm_decode_one_shard", self.X2, self.W2, True)
+        else:
+            row("row_gemm_one_shard", self.X1, self.W1, False)
+            col("column_gemm_allgathered_one_shard", self.Y, self.W3)
+        return ops
 
 
 def traffic_bytes(wid, op):
@@ -144,6 +184,7 @@ def cpu_baseline(wl, rows, np, oracle, torch):
         return oracle.widen_bf16(t.detach().cpu().view(torch.int16).numpy().view(np.uint16))
     P = wl.P
     flops, secs, parity = 0.0, 0.0, {}
+    fold_s, fold_b = 0.0, 0
     for name, fl, _, _ in wl.ops:
         if name in ("column_gemm", "column_gemm_decode"):
             X, W = wl.X1, wl.W1
@@ -165,15 +206,33 @@ def cpu_baseline(wl, rows, np, oracle, torch):
             Y = oracle.fold_f64(parts)
             secs += time.perf_counter() - t0
             flops += fl * r / X.shape[0]
+            # the fp32 fold (and one rounding) of the oracle's own partials
+            p32 = np.stack([p.astype(np.float32) for p in parts])
+            t0 = time.perf_counter()
+            oracle.round_bf16(oracle.fold_f32(p32))
+            fold_s = time.perf_counter() - t0
+            fold_b = p32.nbytes + p32[0].size * 2
             out = {2: "Y2", 3: "Y2", 4: "Y2", 5: "Y"}[wl.wid]
             got = host64(getattr(wl, out)[:r])
             parity[name] = dict(rows=r, rel_l2=oracle.rel_l2(got, Y),
                                 max_abs=oracle.max_abs(got, Y))
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return dict(value=flops / secs / 1e12 if secs > 0 else None, unit="TFLOP/s",
                 cores=oracle.num_threads(), kind="oracle",
                 sample=f"first {rows} token rows of each GEMM (all output columns, all K), "
                        f"fp64 triple loop with explicit shard split/concat/sum; "
-                       f"{flops / 1e9:.1f} GFLOP in {secs:.1f} s"), parity
+                       f"{flops / 1e9:.1f} GFLOP in {secs:.1f} s; linear in the row count, "
+                       f"so the full workload takes about {secs * wl.shape['M'] / min(rows, wl.shape['M']):.0f} s",
+                fold_gbps=fold_b / fold_s / 1e9 if fold_s > 0 else None,
+                cpu_model=cpu_model, os_cpu_count=os.cpu_count(),
+                affinity=len(os.sched_getaffinity(0))), parity
 
 
 def main():
@@ -231,6 +290,36 @@ def main():
             st["frac_hbm_peak"] = st["gbps"] / PEAK_HBM_GBPS
         op_stats[name] = st
 
+    # Context, outside the timed step: each GEMM's shard 0 alone at its real
+    # shape, and a plain device copy of 1 GiB.
+    single = {}
+    for name, fl, nb, fn in wl.single:
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / 10 * 1e3
+        single[name] = dict(avg_us=us, tflops=fl / us / 1e6, gbps=nb / us / 1e3,
+                            frac_bf16_peak=fl / us / 1e6 / PEAK_BF16_TFLOPS,
+                            frac_hbm_peak=nb / us / 1e3 / PEAK_HBM_GBPS)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * (1 << 30) * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+
     # dominant kernel: the op with the most time
     dom = max(op_stats, key=lambda k: op_stats[k]["avg_us"])
     d = op_stats[dom]
@@ -261,6 +350,11 @@ def main():
         "config": dict(workload=wl.name, **wl.shape),
         "roofline": roof,
         "ops": op_stats,
+        "context": {"one_shard": single,
+                    "device_copy_gbps": copy_gbps,
+                    "note": "one_shard: shard 0 of each GEMM launched alone at its real shape "
+                            "(one GPU's share); device_copy_gbps: read+write bytes of a 1 GiB "
+                            "device-to-device copy per second; neither is part of the step"},
     }
     if not args.no_cpu_baseline:
         import oracle
