@@ -13,7 +13,9 @@ Prints ONE JSON line.  `value` is the step's GEMM TFLOP/s; `roofline` is for
 the dominant kernel (the fc1 column GEMM, MFMA-bound), its time measured with
 HIP events on the stream it runs on; `cpu_baseline` times the CPU oracle on a
 bounded sample of the same workload; `context` holds figures taken outside the
-timed step (each GEMM's shard 0 alone at its real shape, a plain device copy).
+timed step (each GEMM's shard 0 alone at its real shape, a plain device copy,
+the shader clock while each GEMM runs and the roofline fraction at that clock:
+the chip lowers its clock under sustained matrix-core load).
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload 2|3|4|5]
 """
@@ -30,6 +32,7 @@ if ROOT not in sys.path:
 METRIC = "TFLOP/s and % bf16 MFMA peak, TP column/row Linear shard GEMM; reduce GB/s"
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 flop/clk/CU, dense
 PEAK_HBM_GBPS = 8000.0
+PEAK_CLOCK_GHZ = 2.4        # the clock the bf16 peak assumes
 
 
 def parse():
@@ -235,6 +238,52 @@ def cpu_baseline(wl, rows, np, oracle, torch):
                 affinity=len(os.sched_getaffinity(0))), parity
 
 
+def shader_clock(wl, op_stats, steps, step_ms, torch):
+    """Shader clock (GHz) with the GPU idle, while each GEMM of the step runs
+    back to back, and over a replay of the timed steps: a probe kernel
+    (libtplclock.so, one wave per block) on a second stream counts s_memtime
+    ticks against the 100 MHz real-time counter over a window of a few ms
+    (the clock swings under load, so short windows mislead).  Outside the
+    timed step; None when the probe library is not built."""
+    import ctypes
+    path = os.path.join(ROOT, "tensor_linear_amd", "libtplclock.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.tp_clock_probe.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_uint,
+                                   ctypes.c_void_p]
+    lib.tp_clock_probe.restype = ctypes.c_int
+    nb, delay_us = 16, 50
+    buf = torch.zeros(2 * nb, dtype=torch.int64, device="cuda:0")
+    side = torch.cuda.Stream()
+
+    def probe(fn, reps, window_us):
+        torch.cuda.synchronize()
+        rc = lib.tp_clock_probe(ctypes.c_void_p(buf.data_ptr()), nb, delay_us * 100,
+                                int(window_us * 100), ctypes.c_void_p(side.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"tp_clock_probe failed: hip error {rc}")
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        o = buf.cpu().tolist()
+        ghz = [o[2 * b] / (o[2 * b + 1] / 100e6) / 1e9 for b in range(nb)]
+        return sum(ghz) / nb
+
+    def step():
+        for op in wl.ops:
+            op[3]()
+
+    out = {"idle": probe(lambda: None, 0, 500)}
+    for name, fl, _, fn in wl.ops:
+        if not fl:
+            continue
+        window = 2500
+        out[name] = probe(fn, int((delay_us + window + 300) / op_stats[name]["avg_us"]) + 2, window)
+    out["step_replay"] = probe(step, steps, max(1000.0, 0.8 * steps * step_ms * 1e3 - delay_us))
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -320,6 +369,8 @@ def main():
     copy_gbps = 2 * (1 << 30) * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst
 
+    clocks = shader_clock(wl, op_stats, args.steps, ms_step, torch)
+
     # dominant kernel: the op with the most time
     dom = max(op_stats, key=lambda k: op_stats[k]["avg_us"])
     d = op_stats[dom]
@@ -352,10 +403,20 @@ def main():
         "ops": op_stats,
         "context": {"one_shard": single,
                     "device_copy_gbps": copy_gbps,
+                    "shader_clock_ghz": clocks,
                     "note": "one_shard: shard 0 of each GEMM launched alone at its real shape "
                             "(one GPU's share); device_copy_gbps: read+write bytes of a 1 GiB "
-                            "device-to-device copy per second; neither is part of the step"},
+                            "device-to-device copy per second; shader_clock_ghz: the shader "
+                            "clock idle, while each GEMM of the step runs back to back (2.5 ms "
+                            "window) and over a replay of the timed steps, from a probe kernel "
+                            "on a second stream; bf16 peak assumes "
+                            f"{PEAK_CLOCK_GHZ} GHz; none of these is part of the step"},
     }
+    if clocks and roof["bound"] == "mfma" and dom in clocks:
+        c = clocks[dom]
+        peak_c = PEAK_BF16_TFLOPS * c / PEAK_CLOCK_GHZ
+        out["context"]["roofline_at_measured_clock"] = dict(
+            kernel=dom, clock_ghz=c, peak=peak_c, unit="TFLOP/s", frac=roof["achieved"] / peak_c)
     if not args.no_cpu_baseline:
         import oracle
         cb, parity = cpu_baseline(wl, args.cpu_rows, np, oracle, torch)

@@ -29,6 +29,16 @@ def test_every_declared_function_is_exported():
         assert hasattr(lib, name), name
 
 
+def test_clock_probe_library_loads():
+    # The bench's shader-clock probe lives in a library of its own; it must
+    # load without a GPU and export its one entry point.
+    path = os.path.join(ROOT, "tensor_linear_amd", "libtplclock.so")
+    if not os.path.exists(path):
+        pytest.skip("libtplclock.so not built")
+    lib = ctypes.CDLL(path)
+    assert hasattr(lib, "tp_clock_probe")
+
+
 def test_status_strings():
     for s in range(9):
         assert tl.tp_status_str(s).startswith("TP_")
