@@ -106,8 +106,14 @@ void gemm_skinny_kernel(GemmArgs g, FoldArgs f) {
                 if (m > g.M - 1) m = g.M - 1;
                 src = (const __bf16 *)g.A + (int64_t)shard * g.a_shard + m * g.lda + k;
             }
-            __builtin_amdgcn_global_load_lds((const void *)src,
-                                             (LDS_PTR(void))(dst + q * 1024), 16, 0, 0);
+            // Written as an instruction the compiler does not track: its own
+            // wait analysis would drain every load in flight before the next
+            // LDS read (it cannot tell which stage a load writes), which
+            // leaves no stage of lead; the waits the pipeline needs are the
+            // explicit ones at the top of each stage.
+            const uint32_t m0v = (uint32_t)(uintptr_t)(dst + q * 1024);
+            asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                         :: "v"(src), "s"(m0v) : "memory", "m0");
         }
         if (++lk == nks) { lk = 0; ++ls; }
     };
@@ -126,9 +132,17 @@ void gemm_skinny_kernel(GemmArgs g, FoldArgs f) {
     const int fk = lane >> 4;     // fragment 8-column group
     int cs = 0, ck = 0;           // compute cursor (shard index, k stage)
     for (int t = 0; t < total; ++t) {
-        // Stage t's loads were issued NST-1 stages ago; NST-2 later stages'
-        // loads may stay in flight.
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW * (NST - 2)) : "memory");
+        // Stage t's loads were issued NST-1 stages ago; the loads of the
+        // later stages issued since (NST-2 of them, fewer in the last stages,
+        // where nothing is issued past the end) may stay in flight.
+        const int later = total - 1 - t;
+        if (later >= NST - 2) {
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW * (NST - 2)) : "memory");
+        } else {
+#pragma unroll
+            for (int r = 0; r < NST - 2; ++r)
+                if (later == r) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW * r) : "memory");
+        }
         __syncthreads();
         issue(t + NST - 1);
         LDS_PTR(char) st = lds + (t % NST) * STB;
@@ -215,13 +229,17 @@ hipError_t launch_gemm_skinny(const GemmArgs &g, int out_type, const FoldArgs *f
                               hipStream_t s) {
     if (g.M == 0 || g.N == 0 || g.P == 0) return hipSuccess;
     // LDS per workgroup: NST * (16 + 16*MB) * KB * 2 bytes, plus the
-    // cross-wave sums.  Two stages; small stages let several workgroups share
-    // a CU, which keeps more loads in flight when the grid is large (one
-    // workgroup per 16 output columns and shard); the fused fold has a P
-    // times smaller grid and streams better with larger stages.
+    // cross-wave sums.  Small stages let several workgroups share a CU, which
+    // keeps more loads in flight when the grid is large (one workgroup per
+    // 16 output columns and shard: three 16 KB stages, two in flight); the
+    // fused fold has a P times smaller grid and streams best with two 32 KB
+    // stages (measured with M = 16, K = 8192, N = 28672 over 8 shards:
+    // column 82-83 us with 3 or 4 stages of 256 columns against 88-89 with 2;
+    // the fused fold of 8 shards of K = 3584, N = 8192: 87 us with 2 x 512,
+    // 93-105 with 256- or 384-column stages).
     if (g.M <= 16) {
         if (fold) return launch_mb<1, 512, 2>(g, out_type, fold, s);   // 64 KB
-        return launch_mb<1, 256, 2>(g, out_type, fold, s);             // 32 KB
+        return launch_mb<1, 256, 3>(g, out_type, fold, s);             // 48 KB
     }
     if (g.M <= 32) return launch_mb<2, 256, 2>(g, out_type, fold, s);  // 48 KB
     return launch_mb<4, 256, 2>(g, out_type, fold, s);                 // 80 KB
