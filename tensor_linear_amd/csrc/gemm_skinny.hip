@@ -3,8 +3,9 @@
 // it streams W from HBM ("模型并行", "Tensor Parallel": Y_i = X W_i for the
 // column form, the partials X_i W_i for the row form).
 //
-// Work unit: one workgroup owns BN = 16 rows of W (16 output columns) and
-// one shard -- or, in the fused row form, all P shards in ascending order.
+// Work unit: one workgroup owns BN = 16*NB rows of W (NB blocks of 16 output
+// columns) and one shard -- or, in the fused row form, all P shards in
+// ascending order; the NB blocks share the staged X rows.
 // W and X move global -> LDS with global_load_lds_dwordx4 in NST stages of
 // KB columns of K; each 1 KB load instruction covers one contiguous KB*2-byte
 // run of one row, so HBM sees long sequential runs rather than 64-byte
@@ -42,11 +43,12 @@ __device__ __forceinline__ void store_out(void *Y, int64_t o, float v) {
     else ((float *)Y)[o] = v;
 }
 
-// MB: 16-row blocks of M.  KB: K columns per stage.  NST: stages.
-template <int MB, int KB, int NST, int OUT, bool FOLD>
+// NB: 16-row blocks of W.  MB: 16-row blocks of M.  KB: K columns per stage.
+// NST: stages.
+template <int NB, int MB, int KB, int NST, int OUT, bool FOLD>
 __global__ __launch_bounds__(SK_THREADS)
 void gemm_skinny_kernel(GemmArgs g, FoldArgs f) {
-    constexpr int BN = SKINNY_BN;          // W rows per workgroup
+    constexpr int BN = 16 * NB;            // W rows per workgroup
     constexpr int XR = 16 * MB;            // X rows staged
     constexpr int ROWB = KB * 2;           // bytes per staged row
     constexpr int CPR = ROWB / 16;         // 16-byte chunks per row
@@ -58,7 +60,7 @@ void gemm_skinny_kernel(GemmArgs g, FoldArgs f) {
     constexpr int SUBS = KB / 32 / 4;      // k32 sub-steps per wave per stage
     static_assert(SUBS >= 1, "KB >= 128");
     __shared__ __attribute__((aligned(1024))) char smem[NST * STB];
-    __shared__ f32x4 red[4][MB][64];
+    __shared__ f32x4 red[4][NB][MB][64];
     LDS_PTR(char) lds = (LDS_PTR(char))smem;
 
     const int tid = threadIdx.x;
@@ -121,12 +123,16 @@ void gemm_skinny_kernel(GemmArgs g, FoldArgs f) {
 #pragma unroll
     for (int t = 0; t < NST - 1; ++t) issue(t);
 
-    f32x4 acc[MB];
+    f32x4 acc[NB][MB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float run[MB];  // running fused sum, output mapping (see below)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) run[mb] = 0.f;
+    for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float run[NB][MB];  // running fused sum, output mapping (see below)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) run[nb][mb] = 0.f;
 
     const int frow = lane & 15;   // fragment row
     const int fk = lane >> 4;     // fragment 8-column group
@@ -151,15 +157,23 @@ void gemm_skinny_kernel(GemmArgs g, FoldArgs f) {
         for (int sub = 0; sub < SUBS; ++sub) {
             const int c = (sub * 4 + wave) * 4 + fk;  // chunk within the stage
             const bool valid = kb + c * 8 < Ks;
-            bf16x8 wv = *(LDS_PTR(bf16x8))(st + frow * ROWB + ((c ^ frow) << 4));
-            if (!valid) wv = bf16x8{};
+            bf16x8 wv[NB], xv[MB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                wv[nb] = *(LDS_PTR(bf16x8))(st + (nb * 16 + frow) * ROWB + ((c ^ frow) << 4));
+                if (!valid) wv[nb] = bf16x8{};
+            }
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 const int xr = BN + mb * 16 + frow;
-                bf16x8 xv = *(LDS_PTR(bf16x8))(st + xr * ROWB + ((c ^ (xr & 15)) << 4));
-                if (!valid) xv = bf16x8{};
-                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv, xv, acc[mb], 0, 0, 0);
+                xv[mb] = *(LDS_PTR(bf16x8))(st + xr * ROWB + ((c ^ (xr & 15)) << 4));
+                if (!valid) xv[mb] = bf16x8{};
             }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv[nb], xv[mb], acc[nb][mb], 0, 0, 0);
         }
         if (++ck < nks) continue;
 
@@ -168,25 +182,29 @@ void gemm_skinny_kernel(GemmArgs g, FoldArgs f) {
         // n%4, block m/16 (16x16 D layout, W rows as the row operand).
         // Thread tid takes n = tid % 16, m = tid / 16 + 16*mb.
 #pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-            red[wave][mb][lane] = acc[mb];
-            acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            red[wave][nb][mb][lane] = acc[nb][mb];
+            acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         __syncthreads();
         const int on = tid & 15, om = tid >> 4;
         const int src_lane = 16 * (on >> 2) + om, src_r = on & 3;
         const int shard = s_begin + cs;
 #pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-            float v = red[0][mb][src_lane][src_r];
-            v = v + red[1][mb][src_lane][src_r];
-            v = v + red[2][mb][src_lane][src_r];
-            v = v + red[3][mb][src_lane][src_r];
-            const int64_t m = om + 16 * mb, n = n0 + on;
+            float v = red[0][nb][mb][src_lane][src_r];
+            v = v + red[1][nb][mb][src_lane][src_r];
+            v = v + red[2][nb][mb][src_lane][src_r];
+            v = v + red[3][nb][mb][src_lane][src_r];
+            const int64_t m = om + 16 * mb, n = n0 + nb * 16 + on;
             if (FOLD) {
-                run[mb] = cs == 0 ? v : run[mb] + v;
+                run[nb][mb] = cs == 0 ? v : run[nb][mb] + v;
                 if (cs == s_count - 1 && m < g.M && n < g.N)
-                    store_out<OUT>(f.Y, m * f.ldy + n, run[mb]);
+                    store_out<OUT>(f.Y, m * f.ldy + n, run[nb][mb]);
             } else if (m < g.M && n < g.N) {
                 store_out<OUT>(g.C, (int64_t)shard * g.c_shard + m * g.ldc + n, v);
             }
@@ -198,19 +216,19 @@ void gemm_skinny_kernel(GemmArgs g, FoldArgs f) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <int MB, int KB, int NST>
+template <int NB, int MB, int KB, int NST>
 hipError_t launch_mb(const GemmArgs &g, int out_type, const FoldArgs *fold, hipStream_t s) {
-    const int64_t tn = (g.N + SKINNY_BN - 1) / SKINNY_BN;
+    const int64_t tn = (g.N + 16 * NB - 1) / (16 * NB);
     const int64_t blocks = fold ? tn : tn * g.P;
     if (blocks > 0x7FFFFFFFll) return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)blocks), block(SK_THREADS);
     FoldArgs f = fold ? *fold : FoldArgs{nullptr, 0, 0};
     if (fold) {
-        if (out_type == OUT_BF16) gemm_skinny_kernel<MB, KB, NST, OUT_BF16, true><<<grid, block, 0, s>>>(g, f);
-        else gemm_skinny_kernel<MB, KB, NST, OUT_F32, true><<<grid, block, 0, s>>>(g, f);
+        if (out_type == OUT_BF16) gemm_skinny_kernel<NB, MB, KB, NST, OUT_BF16, true><<<grid, block, 0, s>>>(g, f);
+        else gemm_skinny_kernel<NB, MB, KB, NST, OUT_F32, true><<<grid, block, 0, s>>>(g, f);
     } else {
-        if (out_type == OUT_BF16) gemm_skinny_kernel<MB, KB, NST, OUT_BF16, false><<<grid, block, 0, s>>>(g, f);
-        else gemm_skinny_kernel<MB, KB, NST, OUT_F32, false><<<grid, block, 0, s>>>(g, f);
+        if (out_type == OUT_BF16) gemm_skinny_kernel<NB, MB, KB, NST, OUT_BF16, false><<<grid, block, 0, s>>>(g, f);
+        else gemm_skinny_kernel<NB, MB, KB, NST, OUT_F32, false><<<grid, block, 0, s>>>(g, f);
     }
     return hipGetLastError();
 }
@@ -228,21 +246,22 @@ bool gemm_skinny_supported(const GemmArgs &g) {
 hipError_t launch_gemm_skinny(const GemmArgs &g, int out_type, const FoldArgs *fold,
                               hipStream_t s) {
     if (g.M == 0 || g.N == 0 || g.P == 0) return hipSuccess;
-    // LDS per workgroup: NST * (16 + 16*MB) * KB * 2 bytes, plus the
+    // LDS per workgroup: NST * (16*NB + 16*MB) * KB * 2 bytes, plus the
     // cross-wave sums.  Small stages let several workgroups share a CU, which
     // keeps more loads in flight when the grid is large (one workgroup per
-    // 16 output columns and shard: three 16 KB stages, two in flight); the
-    // fused fold has a P times smaller grid and streams best with two 32 KB
-    // stages (measured with M = 16, K = 8192, N = 28672 over 8 shards:
-    // column 82-83 us with 3 or 4 stages of 256 columns against 88-89 with 2;
-    // the fused fold of 8 shards of K = 3584, N = 8192: 87 us with 2 x 512,
-    // 93-105 with 256- or 384-column stages).
+    // 16 output columns and shard: three 16 KB stages, two in flight).  The
+    // fused fold has a P times smaller grid: one workgroup per CU with 32
+    // output columns and five 24 KB stages, four in flight.  Measured with
+    // M = 16, K = 8192, N = 28672 over 8 shards: column 82-83 us with 3 or 4
+    // stages of 256 columns against 88-89 with 2; fused fold of 8 shards of
+    // K = 3584, N = 8192: 82-83 us with 32 columns and 3-6 stages, 86-87 with
+    // 16 columns and two 512-column stages.
     if (g.M <= 16) {
-        if (fold) return launch_mb<1, 512, 2>(g, out_type, fold, s);   // 64 KB
-        return launch_mb<1, 256, 3>(g, out_type, fold, s);             // 48 KB
+        if (fold) return launch_mb<2, 1, 256, 5>(g, out_type, fold, s);   // 120 KB
+        return launch_mb<1, 1, 256, 3>(g, out_type, fold, s);             // 48 KB
     }
-    if (g.M <= 32) return launch_mb<2, 256, 2>(g, out_type, fold, s);  // 48 KB
-    return launch_mb<4, 256, 2>(g, out_type, fold, s);                 // 80 KB
+    if (g.M <= 32) return launch_mb<1, 2, 256, 2>(g, out_type, fold, s);  // 48 KB
+    return launch_mb<1, 4, 256, 2>(g, out_type, fold, s);                 // 80 KB
 }
 
 }  // namespace tpl

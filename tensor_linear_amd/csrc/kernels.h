@@ -44,7 +44,6 @@ hipError_t launch_gemm_skinny(const GemmArgs &g, int out_type, const FoldArgs *f
                               hipStream_t s);
 bool gemm_skinny_supported(const GemmArgs &g);
 constexpr int SKINNY_MAX_M = 64;
-constexpr int SKINNY_BN = 16;
 
 // Any shape, stride or alignment; fp32 or bf16 inputs.
 hipError_t launch_gemm_generic(const GemmArgs &g, int in_type, int out_type, hipStream_t s);
