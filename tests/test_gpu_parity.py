@@ -109,6 +109,25 @@ def test_kernel_paths_bitwise(case):
     _run_all_modes(Xd, Wd, X64, Wio, M, K, N, P, torch.bfloat16)
 
 
+# The decode kernel pipelines K in stages (column and partial forms: three
+# stages of 256 columns; fused fold: five).  In the last stages fewer later
+# stages exist, so the waits there differ; these shapes give every count of
+# stages from 1 to 12 per workgroup (K per shard 256*s, P shards walked by
+# the fused form), with and without a ragged last stage, and a fused
+# workgroup whose second 16-column block is partly past N.
+STAGES = [(M, (256 * s + tail) * P, 48, P)
+          for M in (16, 7, 1) for P in (1, 2) for s in (1, 2, 3, 4, 5, 6) for tail in (0, 8)
+          if not (M != 16 and tail)]
+
+
+@pytest.mark.parametrize("case", range(len(STAGES)))
+def test_decode_stage_counts_bitwise(case):
+    M, K, N, P = STAGES[case]
+    print(f"case M={M} K={K} N={N} P={P}", flush=True)
+    Xd, Wd, X64, Wio = _inputs_int(900 + case, M, K, N, torch.bfloat16)
+    _run_all_modes(Xd, Wd, X64, Wio, M, K, N, P, torch.bfloat16)
+
+
 def test_strided_views_bitwise():
     # Leading dims larger than the row width (views into bigger buffers).
     M, K, N, P = 70, 256, 128, 4
