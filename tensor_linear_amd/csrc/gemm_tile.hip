@@ -24,9 +24,14 @@
 // row), so the 16 rows read by one 16-lane group of ds_read_b128 hit 16
 // different 16-byte bank groups.
 //
+// Each tile's first MFMA of every accumulator block takes a zero C operand,
+// so no accumulator registers are cleared between tiles.
+//
 // Edges: rows past M or N are clamped to the last valid row (their results
-// are not stored).  K must be a positive multiple of BK.
+// are not stored).  K must be a positive multiple of BK.  Tiles entirely
+// inside M x N store without per-store bounds tests.
 #include "kernels.h"
+#include <type_traits>
 
 namespace tpl {
 namespace {
@@ -216,14 +221,9 @@ void gemm_tile_kernel(GemmArgs g, TileSched ts, int vec_store) {
     bool drained = true;  // no epilogue store is in flight
     for (int q = 0; q < ntiles; ++q) {
         f32x16 acc[4][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-        for (int kt = 0; kt < nk; ++kt, ++it) {
+        auto kstep = [&](auto first) __attribute__((always_inline)) {
+            constexpr bool FIRST = decltype(first)::value;
             LDS_PTR(char) st = lds + (it % NST) * STAGE;
             LDS_PTR(char) st_next = lds + ((it + 1) % NST) * STAGE;
 #pragma unroll
@@ -261,8 +261,12 @@ void gemm_tile_kernel(GemmArgs g, TileSched ts, int vec_store) {
                     // load of the phase (the compiler drains every LDS read at
                     // such a wait once an LDS-writing load is in flight).
                     const int i = u & 3, j = ((u & 3) + (u >> 2)) & 3;
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][i], xf[cur][j],
-                                                                        acc[i][j], 0, 0, 0);
+                    if (FIRST && ks == 0)   // the tile's first product of each block: C = 0
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][i], xf[cur][j],
+                                                                            f32x16{}, 0, 0, 0);
+                    else
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][i], xf[cur][j],
+                                                                            acc[i][j], 0, 0, 0);
                     if (u < 8) {
                         if (u < 4)
                             wf[nx][u] = *(LDS_PTR(bf16x8))(rd + OPB + wrow_off + u * 32 * ROWB + slot);
@@ -290,7 +294,10 @@ void gemm_tile_kernel(GemmArgs g, TileSched ts, int vec_store) {
             }
             __builtin_amdgcn_sched_barrier(0);
             if (NST != 2) advance();
-        }
+        };
+        kstep(std::true_type{});
+        ++it;
+        for (int kt = 1; kt < nk; ++kt, ++it) kstep(std::false_type{});
 
         // ---- epilogue.  32x32 D layout with W rows as the row operand:
         // lane holds m = lane%32 and, for r4 = 0..3, the 4 columns
@@ -312,46 +319,90 @@ void gemm_tile_kernel(GemmArgs g, TileSched ts, int vec_store) {
             const int64_t tm_w = tm0 + wm * 128, tn_w = tn0 + wn * 128;
             constexpr int VW = OUT == OUT_BF16 ? 8 : 4;   // values per lane store
             constexpr int RPP = 64 * VW / 32;              // rows per pass
+            constexpr int ES = OUT == OUT_BF16 ? 2 : 4;    // bytes per value
+            // Tiles inside M x N (all but the last tile row and column) take a
+            // path without per-store bounds tests: one per-lane byte offset
+            // and a uniform base per store.
+            const bool interior = vec_store && tm0 + TB <= g.M && tn0 + TB <= g.N &&
+                                  (int64_t)RPP * g.ldc * ES < (1ll << 31);
+            if (interior) {
+                const uint32_t lane_off =
+                    (uint32_t)(((int64_t)(lane / (32 / VW)) * g.ldc + VW * (lane % (32 / VW))) * ES);
+                char *wbase = (char *)g.C + (cbase + tm_w * g.ldc + tn_w) * ES;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+                for (int j = 0; j < 4; ++j) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    __builtin_amdgcn_sched_barrier(0);
+                    for (int i = 0; i < 4; ++i) {
+                        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) {
-                        const f32x4 v = {acc[i][j][4 * r4], acc[i][j][4 * r4 + 1],
-                                         acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]};
-                        *(LDS_PTR(f32x4))(ep + frow * EPI_ROWB + (8 * r4 + 4 * fhalf) * 4) = v;
-                    }
-                    const int64_t bm = tm_w + j * 32, bn = tn_w + i * 32;
-#pragma unroll
-                    for (int pp = 0; pp < 32 / RPP; ++pp) {
-                        const int r = pp * RPP + lane / (32 / VW), c = VW * (lane % (32 / VW));
-                        const int64_t m = bm + r, n = bn + c;
-                        float vv[VW];
-#pragma unroll
-                        for (int h = 0; h < VW / 4; ++h) {
-                            const f32x4 a4 = *(LDS_PTR(f32x4))(ep + r * EPI_ROWB + (c + 4 * h) * 4);
-                            vv[4 * h] = a4[0]; vv[4 * h + 1] = a4[1]; vv[4 * h + 2] = a4[2]; vv[4 * h + 3] = a4[3];
+                        for (int r4 = 0; r4 < 4; ++r4) {
+                            const f32x4 v = {acc[i][j][4 * r4], acc[i][j][4 * r4 + 1],
+                                             acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]};
+                            *(LDS_PTR(f32x4))(ep + frow * EPI_ROWB + (8 * r4 + 4 * fhalf) * 4) = v;
                         }
-                        if (m < g.M) {
-                            const int64_t o = cbase + m * g.ldc + n;
-                            if (vec_store && n + VW <= g.N) {
-                                if (OUT == OUT_BF16) {
-                                    bf16x8 hv;
 #pragma unroll
-                                    for (int e = 0; e < 8; ++e) hv[e] = (__bf16)vv[e];
-                                    __builtin_nontemporal_store(hv, (bf16x8 *)((__bf16 *)g.C + o));
-                                } else {
-                                    __builtin_nontemporal_store(f32x4{vv[0], vv[1], vv[2], vv[3]},
-                                                                (f32x4 *)((float *)g.C + o));
-                                }
+                        for (int pp = 0; pp < 32 / RPP; ++pp) {
+                            const int r = pp * RPP + lane / (32 / VW), c = VW * (lane % (32 / VW));
+                            float vv[VW];
+#pragma unroll
+                            for (int h = 0; h < VW / 4; ++h) {
+                                const f32x4 a4 = *(LDS_PTR(f32x4))(ep + r * EPI_ROWB + (c + 4 * h) * 4);
+                                vv[4 * h] = a4[0]; vv[4 * h + 1] = a4[1]; vv[4 * h + 2] = a4[2]; vv[4 * h + 3] = a4[3];
+                            }
+                            char *bp = wbase + ((int64_t)(j * 32 + pp * RPP) * g.ldc + i * 32) * ES + lane_off;
+                            if (OUT == OUT_BF16) {
+                                bf16x8 hv;
+#pragma unroll
+                                for (int e = 0; e < 8; ++e) hv[e] = (__bf16)vv[e];
+                                __builtin_nontemporal_store(hv, (bf16x8 *)bp);
                             } else {
+                                __builtin_nontemporal_store(f32x4{vv[0], vv[1], vv[2], vv[3]}, (f32x4 *)bp);
+                            }
+                        }
+                    }
+                }
+            } else {
 #pragma unroll
-                                for (int e = 0; e < VW; ++e) {
-                                    if (n + e < g.N) {
-                                        if (OUT == OUT_BF16) ((__bf16 *)g.C)[o + e] = (__bf16)vv[e];
-                                        else ((float *)g.C)[o + e] = vv[e];
+                for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int r4 = 0; r4 < 4; ++r4) {
+                            const f32x4 v = {acc[i][j][4 * r4], acc[i][j][4 * r4 + 1],
+                                             acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]};
+                            *(LDS_PTR(f32x4))(ep + frow * EPI_ROWB + (8 * r4 + 4 * fhalf) * 4) = v;
+                        }
+                        const int64_t bm = tm_w + j * 32, bn = tn_w + i * 32;
+#pragma unroll
+                        for (int pp = 0; pp < 32 / RPP; ++pp) {
+                            const int r = pp * RPP + lane / (32 / VW), c = VW * (lane % (32 / VW));
+                            const int64_t m = bm + r, n = bn + c;
+                            float vv[VW];
+#pragma unroll
+                            for (int h = 0; h < VW / 4; ++h) {
+                                const f32x4 a4 = *(LDS_PTR(f32x4))(ep + r * EPI_ROWB + (c + 4 * h) * 4);
+                                vv[4 * h] = a4[0]; vv[4 * h + 1] = a4[1]; vv[4 * h + 2] = a4[2]; vv[4 * h + 3] = a4[3];
+                            }
+                            if (m < g.M) {
+                                const int64_t o = cbase + m * g.ldc + n;
+                                if (vec_store && n + VW <= g.N) {
+                                    if (OUT == OUT_BF16) {
+                                        bf16x8 hv;
+#pragma unroll
+                                        for (int e = 0; e < 8; ++e) hv[e] = (__bf16)vv[e];
+                                        __builtin_nontemporal_store(hv, (bf16x8 *)((__bf16 *)g.C + o));
+                                    } else {
+                                        __builtin_nontemporal_store(f32x4{vv[0], vv[1], vv[2], vv[3]},
+                                                                    (f32x4 *)((float *)g.C + o));
+                                    }
+                                } else {
+#pragma unroll
+                                    for (int e = 0; e < VW; ++e) {
+                                        if (n + e < g.N) {
+                                            if (OUT == OUT_BF16) ((__bf16 *)g.C)[o + e] = (__bf16)vv[e];
+                                            else ((float *)g.C)[o + e] = vv[e];
+                                        }
                                     }
                                 }
                             }
