@@ -26,7 +26,11 @@ Readings where the pages leave a point open (each listed in the design doc):
   * the P partial results are summed in ascending shard order, left to right;
   * the reduce-scatter splits the token dim (dim 0) into P equal row blocks,
     block j going to shard j;
-  * bf16 rounding is round-to-nearest-even.
+  * bf16 rounding is round-to-nearest-even;
+  * the row bias (Partial()) enters the reduced sum once, after the last shard;
+  * a fused gate+up column weight holds, per shard, its gate features first
+    and then its up features; the gated unit is silu(gate) * up;
+  * an embedding id outside [0, V) gives a zero output row.
 
 Arithmetic: inputs (fp32 values or bf16 bit patterns) are widened exactly to
 fp64 and the products are summed in fp64 by orc_dense (oracle.c), k ascending.
@@ -56,7 +60,7 @@ def _load():
     i64, dptr, fptr = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p
     lib.orc_dense.argtypes = [dptr, i64, dptr, i64, dptr, i64, i64, i64, i64]
     lib.orc_dense.restype = None
-    lib.orc_fold_f32.argtypes = [fptr, i64, i64, i64, i64, ctypes.c_int32, fptr, i64]
+    lib.orc_fold_f32.argtypes = [fptr, i64, i64, i64, i64, ctypes.c_int32, fptr, fptr, i64]
     lib.orc_fold_f32.restype = None
     lib.orc_round_bf16.argtypes = [fptr, ctypes.c_void_p, i64]
     lib.orc_round_bf16.restype = None
@@ -168,16 +172,24 @@ def row_parallel_linear(X: np.ndarray, W_io: np.ndarray, P: int) -> np.ndarray:
 # O6: the fp32 shard fold and O9: bf16 rounding (bit-exact references).
 # ---------------------------------------------------------------------------
 
-def fold_f32(partials: np.ndarray) -> np.ndarray:
+def fold_f32(partials: np.ndarray, bias=None) -> np.ndarray:
     """partials: fp32 [P, M, N].  Returns fp32 [M, N] =
-    ((p_0 + p_1) + ...) + p_{P-1}, one fp32 add at a time (oracle.c)."""
+    ((p_0 + p_1) + ...) + p_{P-1}, one fp32 add at a time (oracle.c).
+    bias: None or fp32 [N], the Partial() row bias of the whole layer, added
+    once after the last shard (one more fp32 add)."""
     p = np.ascontiguousarray(partials, dtype=np.float32)
     if p.ndim != 3:
         raise ValueError("partials must be [P, M, N]")
     P, M, N = p.shape
     out = np.empty((M, N), dtype=np.float32)
+    b = None
+    if bias is not None:
+        b = np.ascontiguousarray(bias, dtype=np.float32)
+        if b.shape != (N,):
+            raise ValueError("bias must be [N]")
     if M and N:
-        _load().orc_fold_f32(p.ctypes.data, M * N, N, M, N, P, out.ctypes.data, N)
+        _load().orc_fold_f32(p.ctypes.data, M * N, N, M, N, P,
+                             None if b is None else b.ctypes.data, out.ctypes.data, N)
     return out
 
 
@@ -202,6 +214,101 @@ def reduce_scatter_rows(parts: list, P: int, fold=fold_f64) -> list:
 def all_gather_rows(slices: list) -> np.ndarray:
     """Concatenate the token slices back along dim 0 (Shard(0) -> Replicate)."""
     return np.concatenate(slices, axis=0)
+
+
+# ---------------------------------------------------------------------------
+# Steps next to the Linear: the bias, the gated activation of the fused
+# gate+up column layer, the column layer fed by token slices, and the
+# embedding sharded on its feature dim.
+# ---------------------------------------------------------------------------
+
+def column_parallel_linear_bias(X: np.ndarray, W_io: np.ndarray, b, P: int) -> np.ndarray:
+    """Y_i = X W_i + b_i, concatenated.  The column bias is Shard(0) ("Linear
+    实现解析", tp_shard_type table, row "col"): shard i holds the bias of its
+    own output features, split exactly like W's output dim."""
+    bs = split(np.asarray(b, dtype=np.float64), P, 0)
+    ys = column_shards(X, W_io, P)
+    return np.concatenate([y + bi[None, :] for y, bi in zip(ys, bs)], axis=1)
+
+
+def silu(g: np.ndarray) -> np.ndarray:
+    """silu(g) = g * sigmoid(g) = g / (1 + exp(-g)), fp64.  (For g below about
+    -709, exp(-g) overflows to inf and the quotient is the correct limit, a
+    signed zero.)"""
+    g = np.asarray(g, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """The gated unit of the Llama MLP: silu(gate) * up, fp64."""
+    return silu(g) * np.asarray(u, dtype=np.float64)
+
+
+def column_parallel_gate_up(X: np.ndarray, W_io: np.ndarray, b, P: int):
+    """The gate and up pre-activations of a fused gate+up column layer.
+
+    W_io [K, 2I] is split into P output shards (Column parallel).  Reading
+    of the fused layout: shard i's 2I/P output features hold its I/P gate
+    features first, then its I/P up features, so gate_i and up_i of the same
+    hidden units live on the same shard.  b (None or [2I]) is split the same
+    way.  Returns (G, U), each [M, I], shard i's part at columns
+    [i I/P, (i+1) I/P)."""
+    ys = column_shards(X, W_io, P)
+    if b is not None:
+        bs = split(np.asarray(b, dtype=np.float64), P, 0)
+        ys = [y + bi[None, :] for y, bi in zip(ys, bs)]
+    gs, us = [], []
+    for y in ys:
+        g, u = split(y, 2, 1)
+        gs.append(g)
+        us.append(u)
+    return np.concatenate(gs, axis=1), np.concatenate(us, axis=1)
+
+
+def column_parallel_swiglu(X: np.ndarray, W_io: np.ndarray, b, P: int) -> np.ndarray:
+    """H = silu(G) * U over the shards of a fused gate+up column layer
+    (see column_parallel_gate_up for the layout), [M, I]."""
+    G, U = column_parallel_gate_up(X, W_io, b, P)
+    return swiglu(G, U)
+
+
+def row_parallel_linear_bias(X: np.ndarray, W_io: np.ndarray, b, P: int) -> np.ndarray:
+    """Y = sum_i X_i W_i + b.  The row bias is Partial() ("Linear 实现解析",
+    tp_shard_type table, row "row"): its parts sum to the layer's bias, so
+    the bias enters the reduced output once, added after the shard sum."""
+    return row_parallel_linear(X, W_io, P) + np.asarray(b, dtype=np.float64)[None, :]
+
+
+def column_parallel_linear_gathered(slices: list, W_io: np.ndarray, P: int) -> np.ndarray:
+    """The column layer of the sequence-parallel layout: the P token slices
+    are all-gathered (Shard(0) -> Replicate, O7) into the full X, which then
+    goes through the column-parallel product (nanotron "5.1 TP", column
+    REDUCE_SCATTER mode: all_gather(x) before F.linear)."""
+    return column_parallel_linear(all_gather_rows(slices), W_io, P)
+
+
+def embedding_parallel(ids, E: np.ndarray, P: int) -> np.ndarray:
+    """EmbeddingWithReplicateOutput ("Module 并行：实现 DP/TP/CP/PP 组合",
+    section "DP / TP / CP / PP 并行实现", "Tensor Parallel": the embedding
+    weight is Shard(1) on embedding_dim, the token ids are Replicate, and the
+    output is all-gathered back to Replicate).
+
+    E [V, D] is split into P feature shards E_i [V, D/P] (explicit copies);
+    shard i looks up its rows, Y_i[t] = E_i[ids[t]], and the Y_i are
+    concatenated along the feature dim.  Reading for an id outside [0, V)
+    (the pages do not say): its output row is zero."""
+    ids = np.asarray(ids, dtype=np.int64)
+    V = E.shape[0]
+    outs = []
+    for Ei in split(np.asarray(E), P, 1):
+        Yi = np.zeros((ids.shape[0], Ei.shape[1]), dtype=Ei.dtype)
+        for t in range(ids.shape[0]):
+            v = int(ids[t])
+            if 0 <= v < V:
+                Yi[t] = Ei[v]
+        outs.append(Yi)
+    return np.concatenate(outs, axis=1)
 
 
 # ---------------------------------------------------------------------------

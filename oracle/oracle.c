@@ -59,9 +59,14 @@ void orc_dense(const double *X, int64_t ldx, const double *W, int64_t ldw,
  *   out = ((p_0 + p_1) + p_2) + ... + p_{P-1}
  * one fp32 add at a time.
  *   partials: shard i at partials + i * shard_stride, row stride ldp.
+ * bias (may be NULL): the row-parallel bias, whose placement is Partial()
+ * ("Linear 实现解析", tp_shard_type table, row "row").  Its value is the
+ * bias of the whole layer, so it is added once, to the reduced sum, as one
+ * more fp32 add after the last shard: out = fold + bias[n].
  */
 void orc_fold_f32(const float *partials, int64_t shard_stride, int64_t ldp,
-                  int64_t M, int64_t N, int32_t P, float *out, int64_t ldo)
+                  int64_t M, int64_t N, int32_t P, const float *bias,
+                  float *out, int64_t ldo)
 {
     int64_t m;
 #pragma omp parallel for schedule(static)
@@ -72,6 +77,8 @@ void orc_fold_f32(const float *partials, int64_t shard_stride, int64_t ldp,
                 const float v = partials[(int64_t)i * shard_stride + m * ldp + n];
                 acc = acc + v;
             }
+            if (bias)
+                acc = acc + bias[n];
             out[m * ldo + n] = acc;
         }
     }
