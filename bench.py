@@ -17,7 +17,15 @@ timed step (each GEMM's shard 0 alone at its real shape, a plain device copy,
 the shader clock while each GEMM runs and the roofline fraction at that clock:
 the chip lowers its clock under sustained matrix-core load).
 
-  python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload 2|3|4|5]
+Other workloads (--workload): 3 Llama-70B attention shard, 4 decode, 5
+sequence-parallel round trip, 6 the Llama-8B MLP layer with its column and row
+biases and the gated unit fused into the gate+up column GEMM (the row GEMM
+reads the gated output), 7 the sequence-parallel round trip with the token
+slices in P separate allocations (reduce-scatter writes them, the next column
+GEMM reads them in place), 8 the Llama-8B token embedding sharded on its
+feature dim (P shard tables in separate allocations, all-gathered output).
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload 2..8]
 """
 import argparse
 import json
@@ -40,7 +48,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5, 6, 7, 8])
     ap.add_argument("--cpu-rows", type=int, default=3072,
                     help="rows of X the CPU oracle baseline computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -101,6 +109,43 @@ class Workload:
             self.name = "decode M=16, hidden 8192, intermediate 28672, P=8; column fc1 + " \
                         "row fc2 with the fold fused into the GEMM epilogue"
             self.shape = dict(M=M, hidden=H, intermediate=I, P=P)
+        elif wid == 6:
+            M, H, I = 4096, 4096, 14336
+            self.X1, self.W1 = nb(0, 0, (M, H), sx), nb(0, 1, (2 * I, H), sw)
+            self.b1 = nb(0, 2, (2 * I,), sw)
+            self.W2, self.b2 = nb(1, 1, (H, I), sw), nb(1, 2, (H,), sw)
+            self.H = torch.empty((M, I), dtype=bf, device=dev)
+            self.parts = torch.empty((P, M, H), dtype=torch.float32, device=dev)
+            self.Y2 = torch.empty((M, H), dtype=bf, device=dev)
+            self.ops = [
+                ("column_gemm_swiglu_bias", 2.0 * M * 2 * I * H, None,
+                 lambda: tl.tp_linear_column_ex(self.X1, self.W1, self.H, P, bias=self.b1,
+                                                act=tl.TP_ACT_SWIGLU)),
+                ("row_gemm", 2.0 * M * H * I, None,
+                 lambda: tl.tp_linear_row(self.H, self.W2, self.parts, P, tl.TP_ROW_PARTIAL)),
+                ("shard_fold_bias", 0.0, P * M * H * 4 + M * H * 2 + H * 2,
+                 lambda: tl.tp_shard_reduce_ex(self.parts, self.Y2, P, bias=self.b2)),
+            ]
+            self.name = ("Llama-8B MLP TP layer: M=4096, hidden 4096, intermediate 14336, P=8; "
+                         "fc1 gate+up column 4096->2x14336 with Shard(0) bias and silu(gate)*up "
+                         "fused, fc2 row 14336->4096 on the gated output, fold + Partial bias")
+            self.shape = dict(M=M, hidden=H, intermediate=I, P=P)
+        elif wid == 8:
+            T, V, D = 4096, 128256, 4096
+            Ds = D // P
+            g = torch.Generator(device=dev)
+            g.manual_seed(synth.seed_for(8, 0, 0))
+            self.ids = torch.randint(0, V, (T,), generator=g, device=dev, dtype=torch.int64)
+            self.E = [nb(0, 1 + i, (V, Ds), sx) for i in range(P)]
+            self.Y1 = torch.empty((T, D), dtype=bf, device=dev)
+            self.ops = [
+                ("embedding_lookup_allgather", 0.0, T * D * 2 * 2 + T * 8,
+                 lambda: tl.tp_embedding(self.ids, self.Y1, P, e_shards=self.E)),
+            ]
+            self.name = ("Llama-8B token embedding, EmbeddingWithReplicateOutput: vocab 128256, "
+                         "hidden 4096 Shard(1) over P=8 shard tables, T=4096 token ids, "
+                         "all-gathered output")
+            self.shape = dict(T=T, vocab=V, hidden=D, P=P)
         else:
             M, K, N, N3 = 16384, 28672, 8192, 28672
             self.X1, self.W1 = nb(0, 0, (M, K), sx), nb(0, 1, (N, K), sw)
@@ -108,16 +153,33 @@ class Workload:
             self.parts = torch.empty((P, M, N), dtype=torch.float32, device=dev)
             self.Y = torch.empty((M, N), dtype=bf, device=dev)   # slices = row blocks
             self.Y3 = torch.empty((M, N3), dtype=bf, device=dev)
-            self.ops = [
-                ("row_gemm", 2.0 * M * N * K, None,
-                 lambda: tl.tp_linear_row(self.X1, self.W1, self.parts, P, tl.TP_ROW_PARTIAL)),
-                ("reduce_scatter_fold", 0.0, P * M * N * 4 + M * N * 2,
-                 lambda: tl.tp_shard_reduce(self.parts, self.Y, P, scatter=1)),
-                ("column_gemm_allgathered", 2.0 * M * N3 * N, None,
-                 lambda: tl.tp_linear_column(self.Y, self.W3, self.Y3, P)),
-            ]
-            self.name = "sequence-parallel: M=16384, K=28672 split P=8, N=8192; row GEMM, " \
-                        "reduce-scatter over tokens, all-gather view -> column 8192->28672"
+            if wid == 5:
+                self.ops = [
+                    ("row_gemm", 2.0 * M * N * K, None,
+                     lambda: tl.tp_linear_row(self.X1, self.W1, self.parts, P, tl.TP_ROW_PARTIAL)),
+                    ("reduce_scatter_fold", 0.0, P * M * N * 4 + M * N * 2,
+                     lambda: tl.tp_shard_reduce(self.parts, self.Y, P, scatter=1)),
+                    ("column_gemm_allgathered", 2.0 * M * N3 * N, None,
+                     lambda: tl.tp_linear_column(self.Y, self.W3, self.Y3, P)),
+                ]
+                self.name = "sequence-parallel: M=16384, K=28672 split P=8, N=8192; row GEMM, " \
+                            "reduce-scatter over tokens, all-gather view -> column 8192->28672"
+            else:
+                # Token slices in P separate allocations, as P ranks would hold them.
+                self.slices = [torch.empty((M // P, N), dtype=bf, device=dev) for _ in range(P)]
+                self.ops = [
+                    ("row_gemm", 2.0 * M * N * K, None,
+                     lambda: tl.tp_linear_row(self.X1, self.W1, self.parts, P, tl.TP_ROW_PARTIAL)),
+                    ("reduce_scatter_fold_to_slices", 0.0, P * M * N * 4 + M * N * 2,
+                     lambda: tl.tp_shard_reduce_ex(self.parts, None, P, scatter=1,
+                                                   y_slices=self.slices)),
+                    ("column_gemm_gathered_slices", 2.0 * M * N3 * N, None,
+                     lambda: tl.tp_linear_column_ex(None, self.W3, self.Y3, P,
+                                                    x_slices=self.slices)),
+                ]
+                self.name = "sequence-parallel, slices in separate allocations: M=16384, " \
+                            "K=28672 split P=8, N=8192; row GEMM, reduce-scatter into 8 slice " \
+                            "allocations, column 8192->28672 reading the slices in place"
             self.shape = dict(M=M, K=K, N=N, N_next=N3, P=P)
         self.flops = sum(op[1] for op in self.ops)
         self.single = self._single_shard_ops(P, torch, tl)
@@ -155,7 +217,18 @@ class Workload:
         elif self.wid == 4:
             col("column_gemm_decode_one_shard", self.X1, self.W1)
             row("row_gemm_decode_one_shard", self.X2, self.W2, True)
-        else:
+        elif self.wid == 6:
+            X, W, b = self.X1, self.W1, self.b1
+            Ns = W.shape[0] // P
+            Hs = torch.empty((X.shape[0], Ns // 2), dtype=bf, device=dev)
+            Wi, bi = W[:Ns], b[:Ns]
+            fl = 2.0 * X.shape[0] * Ns * X.shape[1]
+            nb = (Wi.numel() + X.numel() + Hs.numel()) * 2
+            ops.append(("column_gemm_swiglu_bias_one_shard", fl, nb,
+                        lambda: tl.tp_linear_column_ex(X, Wi, Hs, 1, bias=bi,
+                                                       act=tl.TP_ACT_SWIGLU)))
+            row("row_gemm_one_shard", self.H, self.W2, False)
+        elif self.wid in (5, 7):
             row("row_gemm_one_shard", self.X1, self.W1, False)
             col("column_gemm_allgathered_one_shard", self.Y, self.W3)
         return ops
@@ -182,43 +255,72 @@ def traffic_bytes(wid, op):
 
 def cpu_baseline(wl, rows, np, oracle, torch):
     """Time the oracle on the first `rows` token rows of the workload's GEMMs
-    (all output columns), plus the fp32 fold over the same rows."""
+    (all output columns), plus the fp32 fold over the same rows; for the
+    embedding, the oracle's lookup of the first `rows` tokens.  Every oracle
+    input is a workload input (or the oracle's own result of an earlier
+    stage), never a result of the library."""
     def host64(t):
         return oracle.widen_bf16(t.detach().cpu().view(torch.int16).numpy().view(np.uint16))
     P = wl.P
     flops, secs, parity = 0.0, 0.0, {}
     fold_s, fold_b = 0.0, 0
-    for name, fl, _, _ in wl.ops:
-        if name in ("column_gemm", "column_gemm_decode"):
+    emb_b = 0
+    h_oracle = None   # the oracle's own gated output, the input of workload 6's row GEMM
+    for name, fl, nbytes, _ in wl.ops:
+        if name in ("column_gemm", "column_gemm_decode", "column_gemm_swiglu_bias"):
             X, W = wl.X1, wl.W1
             r = min(rows, X.shape[0])
             X64, Wio = host64(X[:r]), np.ascontiguousarray(host64(W).T)
             t0 = time.perf_counter()
-            Y = oracle.column_parallel_linear(X64, Wio, P)
+            if name == "column_gemm_swiglu_bias":
+                Y = oracle.column_parallel_swiglu(X64, Wio, host64(wl.b1), P)
+            else:
+                Y = oracle.column_parallel_linear(X64, Wio, P)
             secs += time.perf_counter() - t0
             flops += fl * r / X.shape[0]
-            got = host64(wl.Y1[:r])
+            out = wl.H if name == "column_gemm_swiglu_bias" else wl.Y1
+            got = host64(out[:r])
+            if name == "column_gemm_swiglu_bias":
+                h_oracle = oracle.widen_bf16(oracle.round_bf16(Y.astype(np.float32)))
             parity[name] = dict(rows=r, rel_l2=oracle.rel_l2(got, Y),
                                 max_abs=oracle.max_abs(got, Y))
         elif name in ("row_gemm", "row_gemm_fused_fold"):
-            X, W = (wl.X2, wl.W2) if wl.wid != 5 else (wl.X1, wl.W1)
-            r = min(rows, X.shape[0])
-            X64, Wio = host64(X[:r]), np.ascontiguousarray(host64(W).T)
+            X, W = (wl.X1, wl.W1) if wl.wid in (5, 7) else (getattr(wl, "X2", None), wl.W2)
+            Mrows = wl.shape["M"]
+            r = min(rows, Mrows)
+            X64 = h_oracle[:r] if wl.wid == 6 else host64(X[:r])
+            Wio = np.ascontiguousarray(host64(W).T)
             t0 = time.perf_counter()
             parts = oracle.row_partials(X64, Wio, P)
             Y = oracle.fold_f64(parts)
+            if wl.wid == 6:
+                Y = Y + host64(wl.b2)[None, :]
             secs += time.perf_counter() - t0
-            flops += fl * r / X.shape[0]
+            flops += fl * r / Mrows
             # the fp32 fold (and one rounding) of the oracle's own partials
             p32 = np.stack([p.astype(np.float32) for p in parts])
             t0 = time.perf_counter()
             oracle.round_bf16(oracle.fold_f32(p32))
             fold_s = time.perf_counter() - t0
             fold_b = p32.nbytes + p32[0].size * 2
-            out = {2: "Y2", 3: "Y2", 4: "Y2", 5: "Y"}[wl.wid]
-            got = host64(getattr(wl, out)[:r])
+            if wl.wid == 7:
+                got_t = torch.cat(wl.slices)[:r]
+            else:
+                got_t = getattr(wl, {5: "Y"}.get(wl.wid, "Y2"))[:r]
+            got = host64(got_t)
             parity[name] = dict(rows=r, rel_l2=oracle.rel_l2(got, Y),
                                 max_abs=oracle.max_abs(got, Y))
+        elif name == "embedding_lookup_allgather":
+            r = min(rows, wl.ids.shape[0])
+            ids = wl.ids[:r].cpu().numpy()
+            E = np.concatenate([t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+                                for t in wl.E], axis=1)
+            t0 = time.perf_counter()
+            Y = oracle.embedding_parallel(ids, E, P)
+            secs += time.perf_counter() - t0
+            emb_b += nbytes * r / wl.ids.shape[0]
+            got = wl.Y1[:r].cpu().view(torch.int16).numpy().view(np.uint16)
+            parity[name] = dict(rows=r, bitwise_equal=bool(np.array_equal(got, Y)))
     cpu_model = ""
     try:
         for line in open("/proc/cpuinfo"):
@@ -227,12 +329,18 @@ def cpu_baseline(wl, rows, np, oracle, torch):
                 break
     except OSError:
         pass
-    return dict(value=flops / secs / 1e12 if secs > 0 else None, unit="TFLOP/s",
+    M = wl.shape.get("M", wl.shape.get("T"))
+    if emb_b:
+        value, unit = emb_b / secs / 1e9 if secs > 0 else None, "GB/s"
+        what = f"lookup of the first {rows} token ids (all shards, all features)"
+    else:
+        value, unit = flops / secs / 1e12 if secs > 0 else None, "TFLOP/s"
+        what = (f"first {rows} token rows of each GEMM (all output columns, all K), fp64 triple "
+                f"loop with explicit shard split/concat/sum; {flops / 1e9:.1f} GFLOP")
+    return dict(value=value, unit=unit,
                 cores=oracle.num_threads(), kind="oracle",
-                sample=f"first {rows} token rows of each GEMM (all output columns, all K), "
-                       f"fp64 triple loop with explicit shard split/concat/sum; "
-                       f"{flops / 1e9:.1f} GFLOP in {secs:.1f} s; linear in the row count, "
-                       f"so the full workload takes about {secs * wl.shape['M'] / min(rows, wl.shape['M']):.0f} s",
+                sample=f"{what} in {secs:.1f} s; linear in the row count, so the full workload "
+                       f"takes about {secs * M / min(rows, M):.0f} s",
                 fold_gbps=fold_b / fold_s / 1e9 if fold_s > 0 else None,
                 cpu_model=cpu_model, os_cpu_count=os.cpu_count(),
                 affinity=len(os.sched_getaffinity(0))), parity
@@ -385,10 +493,15 @@ def main():
                     traffic=traffic_bytes(args.workload, dom),
                     avg_launch_us=d["avg_us"])
 
+    if wl.flops:
+        value, unit = wl.flops / (ms_step * 1e-3) / 1e12, "TFLOP/s"
+    else:   # a pure data-movement workload (the embedding): bytes per second
+        value = sum(op[2] for op in wl.ops) / (ms_step * 1e-3) / 1e9
+        unit = "GB/s"
     out = {
         "metric": METRIC,
-        "value": wl.flops / (ms_step * 1e-3) / 1e12,
-        "unit": "TFLOP/s",
+        "value": value,
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,

@@ -207,6 +207,113 @@ tp_status tp_shard_reduce(const float *partials, int64_t shard_stride, int64_t l
                           int64_t M, int64_t N, int32_t P, int32_t out_dtype,
                           void *stream);
 
+/* Column activations. */
+enum {
+    TP_ACT_NONE = 0,    /* Y = X W_i^T (+ bias)                                   */
+    TP_ACT_SWIGLU = 1   /* the gated unit of a fused gate+up layer, see below      */
+};
+
+/*
+ * tp_linear_column_ex -- tp_linear_column with a bias, the gated activation
+ * of a fused gate+up layer, and an input given as token slices.
+ *
+ * Input: exactly one of X and x_slices is non-NULL.
+ *   X: [M, K] row stride ldx, the full input (as tp_linear_column);
+ *   x_slices: host array of P device pointers; slice j holds rows
+ *     [j*M/P, (j+1)*M/P) of X with row stride ldx, each in its own
+ *     allocation -- the Shard(0) token slices of the sequence-parallel layout
+ *     ("模型并行", "Sequence Parallel": the layout is converted before a
+ *     column layer; nanotron "5.1 TP": the column layer all-gathers x in
+ *     REDUCE_SCATTER mode).  The slices are read in place, so the all-gather
+ *     moves no bytes.  Requires M % P == 0.  The host array is read during
+ *     the call and not kept.
+ * bias: NULL or device [N] of dtype.  The column bias is Shard(0) ("Module
+ *   并行：实现 DP/TP/CP/PP 组合", "Linear 实现解析", tp_shard_type table): shard
+ *   i adds bias[i*N/P + c] to its output feature c, in fp32, before the one
+ *   rounding.
+ * act TP_ACT_NONE: Y as tp_linear_column, plus the bias.
+ * act TP_ACT_SWIGLU: N = 2*I counts the gate and up features, N/P even.
+ *   Shard i's W row block [i*N/P, (i+1)*N/P) holds its I/P gate rows first,
+ *   then the I/P up rows of the same hidden units (the bias likewise).  The
+ *   output is H [M, I]: y_mode TP_Y_CONCAT: ldy >= I, shard i at columns
+ *   [i*I/P, (i+1)*I/P); TP_Y_SHARDS: P blocks [M, I/P] at Y + i*M*ldy,
+ *   ldy >= I/P.  H = silu(G) * U with G, U the fp32 gate and up products
+ *   (plus bias) and silu(g) = g / (1 + e^-g) in fp32; one rounding.
+ * Other arguments and errors as tp_linear_column; also TP_ERR_NULL when both
+ * or neither of X and x_slices are given (K > 0), TP_ERR_INDIVISIBLE when
+ * M % P != 0 with x_slices or (N/P) % 2 != 0 with TP_ACT_SWIGLU, TP_ERR_MODE
+ * for an unknown act.
+ */
+tp_status tp_linear_column_ex(const void *X, const void *const *x_slices, int64_t ldx,
+                              const void *W, int64_t ldw, const void *bias,
+                              void *Y, int64_t ldy, int32_t y_mode, int32_t act,
+                              int64_t M, int64_t N, int64_t K, int32_t P,
+                              int32_t dtype, void *stream);
+
+/*
+ * tp_linear_row_ex -- tp_linear_row with a bias and token slices in separate
+ * allocations.
+ *
+ * bias: NULL or device [N] of dtype.  The row bias is Partial() ("Module
+ *   并行：实现 DP/TP/CP/PP 组合", "Linear 实现解析", tp_shard_type table): its
+ *   parts sum to the layer's bias, so it enters the reduced output once, as
+ *   one fp32 add after the last shard and before the rounding.  Not allowed
+ *   with TP_ROW_PARTIAL (TP_ERR_MODE): there it is the caller's to add.
+ * y_slices: NULL, or for TP_ROW_SCATTER a host array of P device pointers;
+ *   token slice j is written at y_slices[j] with row stride ldy
+ *   (y_slice_stride is then ignored).  TP_ERR_MODE with another mode.
+ * Other arguments and errors as tp_linear_row.
+ */
+tp_status tp_linear_row_ex(const void *X, int64_t ldx, const void *W, int64_t ldw,
+                           const void *bias, void *Y, void *const *y_slices, int64_t ldy,
+                           int64_t y_slice_stride, int32_t mode,
+                           void *workspace, size_t ws_bytes,
+                           int64_t M, int64_t N, int64_t K, int32_t P,
+                           int32_t dtype, void *stream);
+
+/*
+ * tp_shard_reduce_ex -- tp_shard_reduce with the row bias (out_dtype, [N],
+ * added once after the fold; NULL for none) and, for scatter = 1, token
+ * slices in separate allocations (y_slices: NULL, or a host array of P
+ * device pointers, slice j at y_slices[j] with row stride ldy; Y and
+ * y_slice_stride are then ignored and Y may be NULL).  TP_ERR_MODE when
+ * y_slices is given with scatter = 0.
+ */
+tp_status tp_shard_reduce_ex(const float *partials, int64_t shard_stride, int64_t ldp,
+                             const void *bias, void *Y, void *const *y_slices, int64_t ldy,
+                             int64_t y_slice_stride, int32_t scatter,
+                             int64_t M, int64_t N, int32_t P, int32_t out_dtype,
+                             void *stream);
+
+/*
+ * tp_embedding -- EmbeddingWithReplicateOutput ("Module 并行：实现 DP/TP/CP/PP
+ * 组合", "DP / TP / CP / PP 并行实现", "Tensor Parallel": the embedding weight
+ * is Shard(1) on embedding_dim, the token ids are Replicate, and the output
+ * is all-gathered back to Replicate).
+ *
+ * ids: device int64 [T].
+ * Table: exactly one of E and e_shards is non-NULL.
+ *   E: device [V, D] with row stride lde >= D; shard i is its column block
+ *     [i*D/P, (i+1)*D/P) (the Shard(1) views of one allocation);
+ *   e_shards: host array of P device pointers, shard i a [V, D/P] table with
+ *     row stride lde >= D/P in its own allocation (as P ranks would hold it).
+ * Y: y_mode TP_Y_CONCAT: [T, D], ldy >= D, shard i's features at columns
+ *   [i*D/P, (i+1)*D/P) -- the all-gathered, replicated output;
+ *   TP_Y_SHARDS: P blocks [T, D/P] at Y + i*T*ldy, ldy >= D/P -- the Shard(-1)
+ *   output before the all-gather.
+ * Y[t] = row ids[t] of the table, copied bit for bit.  An id outside [0, V)
+ *   gives a zero row and, when bad_flag (device int32) is not NULL, stores 1
+ *   there (the library never clears it).
+ * dtype: TP_BF16 or TP_F32 (table and output).
+ * Errors: TP_ERR_NULL, TP_ERR_SHAPE (negative size, leading dim too small, P
+ * out of range), TP_ERR_INDIVISIBLE (D % P != 0), TP_ERR_DTYPE, TP_ERR_MODE,
+ * TP_ERR_HIP.
+ */
+tp_status tp_embedding(const int64_t *ids, int64_t T, const void *E,
+                       const void *const *e_shards, int64_t lde, int64_t V, int64_t D,
+                       void *Y, int64_t ldy, int32_t y_mode, int32_t P, int32_t dtype,
+                       int32_t *bad_flag, void *stream);
+
 /* Bytes of workspace tp_linear_row needs for (mode, M, N, P); 0 for
  * TP_ROW_PARTIAL, and for invalid arguments. */
 size_t tp_row_workspace_bytes(int32_t mode, int64_t M, int64_t N, int32_t P);

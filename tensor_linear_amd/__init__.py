@@ -47,9 +47,11 @@ TP_F32, TP_BF16 = 0, 1
 TP_REPLICATE, TP_SHARD, TP_PARTIAL = 0, 1, 2
 TP_Y_CONCAT, TP_Y_SHARDS = 0, 1
 TP_ROW_PARTIAL, TP_ROW_SUM, TP_ROW_FUSED, TP_ROW_SCATTER = 0, 1, 2, 3
+TP_ACT_NONE, TP_ACT_SWIGLU = 0, 1
 TP_MAX_SHARDS = 64
 
 EXPORTS = ("tp_shard_layout", "tp_linear_column", "tp_linear_row", "tp_shard_reduce",
+           "tp_linear_column_ex", "tp_linear_row_ex", "tp_shard_reduce_ex", "tp_embedding",
            "tp_row_workspace_bytes", "tp_workspace_zero", "tp_status_str", "tp_version")
 
 
@@ -78,6 +80,18 @@ def _declare(lib):
     lib.tp_shard_reduce.argtypes = [_ptr, _i64, _i64, _ptr, _i64, _i64, _i32, _i64, _i64, _i32,
                                     _i32, _ptr]
     lib.tp_shard_reduce.restype = _i32
+    lib.tp_linear_column_ex.argtypes = [_ptr, _ptr, _i64, _ptr, _i64, _ptr, _ptr, _i64, _i32,
+                                        _i32, _i64, _i64, _i64, _i32, _i32, _ptr]
+    lib.tp_linear_column_ex.restype = _i32
+    lib.tp_linear_row_ex.argtypes = [_ptr, _i64, _ptr, _i64, _ptr, _ptr, _ptr, _i64, _i64, _i32,
+                                     _ptr, _sz, _i64, _i64, _i64, _i32, _i32, _ptr]
+    lib.tp_linear_row_ex.restype = _i32
+    lib.tp_shard_reduce_ex.argtypes = [_ptr, _i64, _i64, _ptr, _ptr, _ptr, _i64, _i64, _i32,
+                                       _i64, _i64, _i32, _i32, _ptr]
+    lib.tp_shard_reduce_ex.restype = _i32
+    lib.tp_embedding.argtypes = [_ptr, _i64, _ptr, _ptr, _i64, _i64, _i64, _ptr, _i64, _i32,
+                                 _i32, _i32, _ptr, _ptr]
+    lib.tp_embedding.restype = _i32
     lib.tp_row_workspace_bytes.argtypes = [_i32, _i64, _i64, _i32]
     lib.tp_row_workspace_bytes.restype = _sz
     lib.tp_workspace_zero.argtypes = [_ptr, _sz, _ptr]
@@ -139,6 +153,23 @@ def _mat(t, name):
     # output); otherwise its leading dim is its width.
     ld = t.stride(0) if t.shape[0] > 1 or t.stride(0) >= t.shape[1] else t.shape[1]
     return t.data_ptr(), t.shape[0], t.shape[1], max(ld, t.shape[1], 1)
+
+
+def _ptr_array(ts, name):
+    """Host array of the data pointers of a list of tensors (or None)."""
+    if ts is None:
+        return None
+    return (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+
+
+def _bias_ptr(bias, dt):
+    if bias is None:
+        return None
+    if bias.dim() != 1 or (bias.numel() > 1 and bias.stride(0) != 1):
+        raise ValueError("bias must be a contiguous 1-D tensor")
+    if _dtype_code(bias) != dt:
+        raise TypeError("bias must have the output dtype")
+    return bias.data_ptr()
 
 
 def _stream(t, stream):
@@ -239,3 +270,165 @@ def tp_shard_reduce(partials, Y, P: int, scatter: int = 0, y_slice_stride: int =
     yp, _, _, ldy = _mat(Y, "Y")
     check(_get_lib().tp_shard_reduce(partials.data_ptr(), ss, ldp, yp, ldy, y_slice_stride, scatter,
                               M, N, P, _dtype_code(Y), _stream(partials, stream)))
+
+
+def tp_linear_column_ex(X, W, Y, P: int, y_mode: int = TP_Y_CONCAT, bias=None,
+                        act: int = TP_ACT_NONE, x_slices=None, stream=None) -> None:
+    """Column-parallel Linear with a bias, the gated unit and token-slice
+    input.  Exactly one of X ([M, K]) and x_slices (P tensors [M/P, K] with
+    one row stride) is given.  W [N, K]; bias [N] or None.  Output columns per
+    shard On = N/P, or N/(2P) with TP_ACT_SWIGLU; Y [M, P*On] for TP_Y_CONCAT
+    or [P, M, On] for TP_Y_SHARDS."""
+    if (X is None) == (x_slices is None):
+        raise ValueError("give exactly one of X and x_slices")
+    if X is not None:
+        xp, M, K, ldx = _mat(X, "X")
+        ref = X
+        sl = None
+    else:
+        if len(x_slices) != P:
+            raise ValueError(f"x_slices must hold P={P} tensors")
+        _, ms, K, ldx = _mat(x_slices[0], "x_slices[0]")
+        for j, t in enumerate(x_slices):
+            _, mj, kj, lj = _mat(t, f"x_slices[{j}]")
+            if (mj, kj) != (ms, K) or (mj > 1 and lj != ldx):
+                raise ValueError("token slices must share shape and row stride")
+            if _dtype_code(t) != _dtype_code(x_slices[0]):
+                raise TypeError("token slices must share one dtype")
+        M, xp, ref = ms * P, None, x_slices[0]
+        sl = _ptr_array(x_slices, "x_slices")
+    wp, N, Kw, ldw = _mat(W, "W")
+    if Kw != K:
+        raise ValueError(f"X has K={K} but W has K={Kw}")
+    dt = _dtype_code(ref)
+    if _dtype_code(W) != dt or _dtype_code(Y) != dt:
+        raise TypeError("X, W and Y must share one dtype")
+    if y_mode == TP_Y_SHARDS:
+        if Y.dim() != 3 or Y.shape[0] != P or Y.shape[1] != M:
+            raise ValueError("Y must be [P, M, On] for TP_Y_SHARDS")
+        yp, _, _, ldy = _mat(Y[0], "Y[0]")
+        if P > 1 and Y.stride(0) != M * ldy:
+            raise ValueError("Y blocks must be M*ldy elements apart")
+        yp = Y.data_ptr()
+    else:
+        yp, _, _, ldy = _mat(Y, "Y")
+    check(_get_lib().tp_linear_column_ex(xp, sl, ldx, wp, ldw, _bias_ptr(bias, dt), yp, ldy,
+                                         y_mode, act, M, N, K, P, dt, _stream(ref, stream)))
+
+
+def tp_linear_row_ex(X, W, Y, P: int, mode: int = TP_ROW_SUM, workspace=None, bias=None,
+                     y_slices=None, y_slice_stride: int = 0, stream=None) -> None:
+    """Row-parallel Linear with the row bias (added once after the fold) and,
+    for TP_ROW_SCATTER, token slices in separate tensors (y_slices: P tensors
+    [M/P, N] with one row stride; Y is then None).  Otherwise as
+    tp_linear_row."""
+    xp, M, K, ldx = _mat(X, "X")
+    wp, N, Kw, ldw = _mat(W, "W")
+    if Kw != K:
+        raise ValueError(f"X has K={K} but W has K={Kw}")
+    dt = _dtype_code(X)
+    if _dtype_code(W) != dt:
+        raise TypeError("X and W must share one dtype")
+    ys = None
+    if y_slices is not None:
+        if Y is not None:
+            raise ValueError("give Y or y_slices, not both")
+        if len(y_slices) != P:
+            raise ValueError(f"y_slices must hold P={P} tensors")
+        _, _, _, ldy = _mat(y_slices[0], "y_slices[0]")
+        for j, t in enumerate(y_slices):
+            _, mj, nj, lj = _mat(t, f"y_slices[{j}]")
+            if (mj, nj) != (M // P, N) or (mj > 1 and lj != ldy) or _dtype_code(t) != dt:
+                raise ValueError("y_slices must be [M/P, N] of the input dtype, one row stride")
+        yp, ys = None, _ptr_array(y_slices, "y_slices")
+    elif mode == TP_ROW_PARTIAL:
+        import torch
+        if Y.dtype != torch.float32 or Y.dim() != 3 or Y.shape[0] != P:
+            raise ValueError("Y must be float32 [P, M, N] for TP_ROW_PARTIAL")
+        _, _, _, ldy = _mat(Y[0], "Y[0]")
+        if P > 1 and Y.stride(0) != M * ldy:
+            raise ValueError("Y parts must be M*ldy elements apart")
+        yp = Y.data_ptr()
+    else:
+        if _dtype_code(Y) != dt:
+            raise TypeError("Y must have the dtype of X")
+        yp, _, _, ldy = _mat(Y, "Y")
+    if workspace is not None:
+        wsp, wsb = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    else:
+        wsp, wsb = None, 0
+    check(_get_lib().tp_linear_row_ex(xp, ldx, wp, ldw, _bias_ptr(bias, dt), yp, ys, ldy,
+                                      y_slice_stride, mode, wsp, wsb, M, N, K, P, dt,
+                                      _stream(X, stream)))
+
+
+def tp_shard_reduce_ex(partials, Y, P: int, scatter: int = 0, bias=None, y_slices=None,
+                       y_slice_stride: int = 0, stream=None) -> None:
+    """tp_shard_reduce with the row bias and, for scatter=1, token slices in
+    separate tensors (y_slices: P tensors [M/P, N], one row stride; Y None)."""
+    import torch
+    if partials.dtype != torch.float32 or partials.dim() != 3 or partials.shape[0] != P:
+        raise ValueError("partials must be float32 [P, M, N]")
+    _, M, N, ldp = _mat(partials[0], "partials[0]")
+    ss = partials.stride(0) if P > 1 else M * ldp
+    if y_slices is not None:
+        if Y is not None:
+            raise ValueError("give Y or y_slices, not both")
+        if len(y_slices) != P:
+            raise ValueError(f"y_slices must hold P={P} tensors")
+        _, _, _, ldy = _mat(y_slices[0], "y_slices[0]")
+        odt = _dtype_code(y_slices[0])
+        for j, t in enumerate(y_slices):
+            _, mj, nj, lj = _mat(t, f"y_slices[{j}]")
+            if (mj, nj) != (M // P, N) or (mj > 1 and lj != ldy) or _dtype_code(t) != odt:
+                raise ValueError("y_slices must be [M/P, N] of one dtype and row stride")
+        yp, ys = None, _ptr_array(y_slices, "y_slices")
+    else:
+        yp, _, _, ldy = _mat(Y, "Y")
+        odt, ys = _dtype_code(Y), None
+    check(_get_lib().tp_shard_reduce_ex(partials.data_ptr(), ss, ldp, _bias_ptr(bias, odt), yp,
+                                        ys, ldy, y_slice_stride, scatter, M, N, P, odt,
+                                        _stream(partials, stream)))
+
+
+def tp_embedding(ids, Y, P: int, E=None, e_shards=None, y_mode: int = TP_Y_CONCAT, bad=None,
+                 stream=None) -> None:
+    """Feature-sharded embedding lookup (EmbeddingWithReplicateOutput).
+    ids: int64 [T].  Exactly one of E ([V, D]) and e_shards (P tensors
+    [V, D/P], one row stride).  Y: [T, D] (TP_Y_CONCAT) or [P, T, D/P]
+    (TP_Y_SHARDS).  bad: None or an int32 tensor set to 1 when an id is
+    outside [0, V) (its output row is zero)."""
+    import torch
+    if ids.dtype != torch.int64 or ids.dim() != 1 or (ids.numel() > 1 and ids.stride(0) != 1):
+        raise ValueError("ids must be a contiguous int64 [T] tensor")
+    T = ids.shape[0]
+    if (E is None) == (e_shards is None):
+        raise ValueError("give exactly one of E and e_shards")
+    if E is not None:
+        ep, V, D, lde = _mat(E, "E")
+        dt, es = _dtype_code(E), None
+    else:
+        if len(e_shards) != P:
+            raise ValueError(f"e_shards must hold P={P} tensors")
+        _, V, Ds, lde = _mat(e_shards[0], "e_shards[0]")
+        dt = _dtype_code(e_shards[0])
+        for i, t in enumerate(e_shards):
+            _, vi, di, li = _mat(t, f"e_shards[{i}]")
+            if (vi, di) != (V, Ds) or (vi > 1 and li != lde) or _dtype_code(t) != dt:
+                raise ValueError("e_shards must share shape, dtype and row stride")
+        ep, D, es = None, Ds * P, _ptr_array(e_shards, "e_shards")
+    if _dtype_code(Y) != dt:
+        raise TypeError("Y must have the table's dtype")
+    if y_mode == TP_Y_SHARDS:
+        if Y.dim() != 3 or Y.shape[0] != P or Y.shape[1] != T:
+            raise ValueError("Y must be [P, T, D/P] for TP_Y_SHARDS")
+        _, _, _, ldy = _mat(Y[0], "Y[0]")
+        if P > 1 and Y.stride(0) != T * ldy:
+            raise ValueError("Y blocks must be T*ldy elements apart")
+        yp = Y.data_ptr()
+    else:
+        yp, _, _, ldy = _mat(Y, "Y")
+    if bad is not None and (bad.dtype != torch.int32 or bad.numel() < 1):
+        raise ValueError("bad must be an int32 tensor")
+    check(_get_lib().tp_embedding(ids.data_ptr(), T, ep, es, lde, V, D, yp, ldy, y_mode, P, dt,
+                                  None if bad is None else bad.data_ptr(), _stream(ids, stream)))

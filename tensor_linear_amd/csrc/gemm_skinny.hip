@@ -25,6 +25,13 @@
 // partials and running the fold kernel, so the result is bitwise equal to
 // that unfused sequence.  No workspace, counter or cross-workgroup signal is
 // needed.
+//
+// Epilogue options: the column bias (Shard(0)) is added to each output in
+// fp32 before rounding; the row bias (Partial(), the whole layer's bias) is
+// added once to the fused sum after the last shard.  The gated unit of a
+// fused gate+up column layer (SWIGLU) takes 16 gate rows and the 16 up rows
+// of the same hidden units per workgroup (NB = 2), so both products of an
+// output land in the same thread's reduction: silu(g + bg) * (u + bu).
 #include "kernels.h"
 
 namespace tpl {
@@ -45,10 +52,12 @@ __device__ __forceinline__ void store_out(void *Y, int64_t o, float v) {
 
 // NB: 16-row blocks of W.  MB: 16-row blocks of M.  KB: K columns per stage.
 // NST: stages.
-template <int NB, int MB, int KB, int NST, int OUT, bool FOLD>
+template <int NB, int MB, int KB, int NST, int OUT, bool FOLD, bool SWIGLU>
 __global__ __launch_bounds__(SK_THREADS)
-void gemm_skinny_kernel(GemmArgs g, FoldArgs f) {
+void gemm_skinny_kernel(GemmArgs g, FoldArgs f, GemmExtra ex) {
+    static_assert(!SWIGLU || (NB == 2 && !FOLD), "gated unit: 16 gate + 16 up rows, column form");
     constexpr int BN = 16 * NB;            // W rows per workgroup
+    constexpr int ON = SWIGLU ? 16 : BN;   // output columns per workgroup
     constexpr int XR = 16 * MB;            // X rows staged
     constexpr int ROWB = KB * 2;           // bytes per staged row
     constexpr int CPR = ROWB / 16;         // 16-byte chunks per row
@@ -73,7 +82,7 @@ void gemm_skinny_kernel(GemmArgs g, FoldArgs f) {
     } else {
         tn = blockIdx.x / g.P; s_begin = blockIdx.x - tn * g.P; s_count = 1;
     }
-    const int64_t n0 = (int64_t)tn * BN;
+    const int64_t n0 = (int64_t)tn * ON;
     const int64_t Ks = g.K;
     const int nks = (int)((Ks + KB - 1) / KB);  // stages per shard
     const int total = s_count * nks;
@@ -100,8 +109,9 @@ void gemm_skinny_kernel(GemmArgs g, FoldArgs f) {
             if (k >= Ks) k = 0;
             const __bf16 *src;
             if (row < BN) {
-                int64_t n = n0 + row;
+                int64_t n = n0 + (SWIGLU ? (row & 15) : row);
                 if (n > g.N - 1) n = g.N - 1;
+                if (SWIGLU && row >= 16) n += ex.up_off;   // the up row of the same unit
                 src = (const __bf16 *)g.B + (int64_t)shard * g.b_shard + n * g.ldb + k;
             } else {
                 int64_t m = row - BN;
@@ -192,21 +202,49 @@ void gemm_skinny_kernel(GemmArgs g, FoldArgs f) {
         const int on = tid & 15, om = tid >> 4;
         const int src_lane = 16 * (on >> 2) + om, src_r = on & 3;
         const int shard = s_begin + cs;
+        const __bf16 *bb = (const __bf16 *)ex.bias;
+        if (SWIGLU) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+            for (int mb = 0; mb < MB; ++mb) {
+                float gv = red[0][0][mb][src_lane][src_r];
+                gv = gv + red[1][0][mb][src_lane][src_r];
+                gv = gv + red[2][0][mb][src_lane][src_r];
+                gv = gv + red[3][0][mb][src_lane][src_r];
+                float uv = red[0][1][mb][src_lane][src_r];
+                uv = uv + red[1][1][mb][src_lane][src_r];
+                uv = uv + red[2][1][mb][src_lane][src_r];
+                uv = uv + red[3][1][mb][src_lane][src_r];
+                const int64_t m = om + 16 * mb, n = n0 + on;
+                if (m < g.M && n < g.N) {
+                    if (bb) {
+                        const __bf16 *bs = bb + (int64_t)shard * ex.bias_shard;
+                        gv = gv + (float)bs[n];
+                        uv = uv + (float)bs[ex.up_off + n];
+                    }
+                    store_out<OUT>(g.C, (int64_t)shard * g.c_shard + m * g.ldc + n, silu_f32(gv) * uv);
+                }
+            }
+        } else {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            float v = red[0][nb][mb][src_lane][src_r];
-            v = v + red[1][nb][mb][src_lane][src_r];
-            v = v + red[2][nb][mb][src_lane][src_r];
-            v = v + red[3][nb][mb][src_lane][src_r];
-            const int64_t m = om + 16 * mb, n = n0 + nb * 16 + on;
-            if (FOLD) {
-                run[nb][mb] = cs == 0 ? v : run[nb][mb] + v;
-                if (cs == s_count - 1 && m < g.M && n < g.N)
-                    store_out<OUT>(f.Y, m * f.ldy + n, run[nb][mb]);
-            } else if (m < g.M && n < g.N) {
-                store_out<OUT>(g.C, (int64_t)shard * g.c_shard + m * g.ldc + n, v);
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                float v = red[0][nb][mb][src_lane][src_r];
+                v = v + red[1][nb][mb][src_lane][src_r];
+                v = v + red[2][nb][mb][src_lane][src_r];
+                v = v + red[3][nb][mb][src_lane][src_r];
+                const int64_t m = om + 16 * mb, n = n0 + nb * 16 + on;
+                if (FOLD) {
+                    run[nb][mb] = cs == 0 ? v : run[nb][mb] + v;
+                    if (cs == s_count - 1 && m < g.M && n < g.N) {
+                        float y = run[nb][mb];
+                        if (bb) y = y + (float)bb[n];     // row bias: once, after the fold
+                        store_out<OUT>(f.Y, m * f.ldy + n, y);
+                    }
+                } else if (m < g.M && n < g.N) {
+                    if (bb) v = v + (float)bb[(int64_t)shard * ex.bias_shard + n];
+                    store_out<OUT>(g.C, (int64_t)shard * g.c_shard + m * g.ldc + n, v);
+                }
             }
         }
         ck = 0;
@@ -216,19 +254,25 @@ void gemm_skinny_kernel(GemmArgs g, FoldArgs f) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <int NB, int MB, int KB, int NST>
-hipError_t launch_mb(const GemmArgs &g, int out_type, const FoldArgs *fold, hipStream_t s) {
-    const int64_t tn = (g.N + 16 * NB - 1) / (16 * NB);
+template <int NB, int MB, int KB, int NST, bool SWIGLU = false>
+hipError_t launch_mb(const GemmArgs &g, int out_type, const FoldArgs *fold, const GemmExtra &ex,
+                     hipStream_t s) {
+    constexpr int ON = SWIGLU ? 16 : 16 * NB;
+    const int64_t tn = (g.N + ON - 1) / ON;
     const int64_t blocks = fold ? tn : tn * g.P;
     if (blocks > 0x7FFFFFFFll) return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)blocks), block(SK_THREADS);
     FoldArgs f = fold ? *fold : FoldArgs{nullptr, 0, 0};
-    if (fold) {
-        if (out_type == OUT_BF16) gemm_skinny_kernel<NB, MB, KB, NST, OUT_BF16, true><<<grid, block, 0, s>>>(g, f);
-        else gemm_skinny_kernel<NB, MB, KB, NST, OUT_F32, true><<<grid, block, 0, s>>>(g, f);
+    if (SWIGLU) {
+        if (fold) return hipErrorInvalidValue;
+        if (out_type == OUT_BF16) gemm_skinny_kernel<NB, MB, KB, NST, OUT_BF16, false, SWIGLU><<<grid, block, 0, s>>>(g, f, ex);
+        else gemm_skinny_kernel<NB, MB, KB, NST, OUT_F32, false, SWIGLU><<<grid, block, 0, s>>>(g, f, ex);
+    } else if (fold) {
+        if (out_type == OUT_BF16) gemm_skinny_kernel<NB, MB, KB, NST, OUT_BF16, true, false><<<grid, block, 0, s>>>(g, f, ex);
+        else gemm_skinny_kernel<NB, MB, KB, NST, OUT_F32, true, false><<<grid, block, 0, s>>>(g, f, ex);
     } else {
-        if (out_type == OUT_BF16) gemm_skinny_kernel<NB, MB, KB, NST, OUT_BF16, false><<<grid, block, 0, s>>>(g, f);
-        else gemm_skinny_kernel<NB, MB, KB, NST, OUT_F32, false><<<grid, block, 0, s>>>(g, f);
+        if (out_type == OUT_BF16) gemm_skinny_kernel<NB, MB, KB, NST, OUT_BF16, false, false><<<grid, block, 0, s>>>(g, f, ex);
+        else gemm_skinny_kernel<NB, MB, KB, NST, OUT_F32, false, false><<<grid, block, 0, s>>>(g, f, ex);
     }
     return hipGetLastError();
 }
@@ -237,15 +281,19 @@ inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 }  // namespace
 
-bool gemm_skinny_supported(const GemmArgs &g) {
+bool gemm_skinny_supported(const GemmArgs &g, const GemmExtra *ex) {
+    if (ex && ex->x_rows > 0) return false;
     return g.M >= 1 && g.M <= SKINNY_MAX_M && g.K > 0 && g.K % 8 == 0 && g.lda % 8 == 0 &&
            g.ldb % 8 == 0 && g.a_shard % 8 == 0 && g.b_shard % 8 == 0 &&
            aligned16(g.A) && aligned16(g.B);
 }
 
 hipError_t launch_gemm_skinny(const GemmArgs &g, int out_type, const FoldArgs *fold,
-                              hipStream_t s) {
+                              const GemmExtra *exp, hipStream_t s) {
     if (g.M == 0 || g.N == 0 || g.P == 0) return hipSuccess;
+    GemmExtra ex{};
+    if (exp) ex = *exp;
+    if (ex.x_rows > 0) return hipErrorInvalidValue;
     // LDS per workgroup: NST * (16*NB + 16*MB) * KB * 2 bytes, plus the
     // cross-wave sums.  Small stages let several workgroups share a CU, which
     // keeps more loads in flight when the grid is large (one workgroup per
@@ -255,13 +303,20 @@ hipError_t launch_gemm_skinny(const GemmArgs &g, int out_type, const FoldArgs *f
     // M = 16, K = 8192, N = 28672 over 8 shards: column 82-83 us with 3 or 4
     // stages of 256 columns against 88-89 with 2; fused fold of 8 shards of
     // K = 3584, N = 8192: 82-83 us with 32 columns and 3-6 stages, 86-87 with
-    // 16 columns and two 512-column stages.
-    if (g.M <= 16) {
-        if (fold) return launch_mb<2, 1, 256, 5>(g, out_type, fold, s);   // 120 KB
-        return launch_mb<1, 1, 256, 3>(g, out_type, fold, s);             // 48 KB
+    // 16 columns and two 512-column stages.  The gated unit streams 32 W rows
+    // (16 gate, 16 up) per workgroup with the column form's stages.
+    if (ex.act == ACT_SWIGLU) {
+        if (fold) return hipErrorInvalidValue;
+        if (g.M <= 16) return launch_mb<2, 1, 256, 3, true>(g, out_type, fold, ex, s);   // 72 KB
+        if (g.M <= 32) return launch_mb<2, 2, 256, 2, true>(g, out_type, fold, ex, s);   // 64 KB
+        return launch_mb<2, 4, 256, 2, true>(g, out_type, fold, ex, s);                  // 96 KB
     }
-    if (g.M <= 32) return launch_mb<1, 2, 256, 2>(g, out_type, fold, s);  // 48 KB
-    return launch_mb<1, 4, 256, 2>(g, out_type, fold, s);                 // 80 KB
+    if (g.M <= 16) {
+        if (fold) return launch_mb<2, 1, 256, 5>(g, out_type, fold, ex, s);   // 120 KB
+        return launch_mb<1, 1, 256, 3>(g, out_type, fold, ex, s);             // 48 KB
+    }
+    if (g.M <= 32) return launch_mb<1, 2, 256, 2>(g, out_type, fold, ex, s);  // 48 KB
+    return launch_mb<1, 4, 256, 2>(g, out_type, fold, ex, s);                 // 80 KB
 }
 
 }  // namespace tpl

@@ -30,6 +30,17 @@
 // Edges: rows past M or N are clamped to the last valid row (their results
 // are not stored).  K must be a positive multiple of BK.  Tiles entirely
 // inside M x N store without per-store bounds tests.
+//
+// Epilogue options (template EPI): EPI_BIAS adds the column bias (Shard(0),
+// "Module 并行：实现 DP/TP/CP/PP 组合", "Linear 实现解析") to the fp32
+// accumulators before rounding; EPI_SWIGLU is the gated unit of a fused
+// gate+up column layer: the W tile's 256 rows are 128 gate rows and the 128
+// up rows of the same hidden units, placed so that each wave's MFMA blocks
+// 0-1 hold gate and blocks 2-3 the matching up features in the same lanes;
+// the output tile is 256 tokens x 128 hidden units, silu(g + bg) * (u + bu).
+// XG: the X rows come from token slices in separate allocations (the
+// all-gather of the sequence-parallel layout read in place); a tile never
+// spans two slices, so only its base pointer changes.
 #include "kernels.h"
 #include <type_traits>
 
@@ -43,9 +54,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_PTR(T) __attribute__((address_space(3))) T *
 
-constexpr int TB = 256;  // tile edge in M and N
+constexpr int TB = 256;  // tile edge in M and N (W rows)
 constexpr int TT = 256;  // threads
 constexpr int GROUP_M = 8;
+
+enum { EPI_NONE = 0, EPI_BIAS = 1, EPI_SWIGLU = 2 };
 
 struct TileSched {
     int tiles_m, tiles_n;  // per shard
@@ -83,9 +96,11 @@ __device__ __forceinline__ int tile_of(const TileSched &ts, int q) {
     return t < ts.T ? t : -1;
 }
 
-template <int BK, int NST, int OUT>
+template <int BK, int NST, int OUT, int EPI, bool XG>
 __global__ __attribute__((amdgpu_flat_work_group_size(TT, TT), amdgpu_waves_per_eu(1, 1)))
-void gemm_tile_kernel(GemmArgs g, TileSched ts, int vec_store) {
+void gemm_tile_kernel(GemmArgs g, TileSched ts, int vec_store, GemmExtra ex) {
+    constexpr bool SWIGLU = EPI == EPI_SWIGLU;
+    constexpr int TBN = SWIGLU ? TB / 2 : TB;   // output columns per tile
     constexpr int ROWB = BK * 2;          // LDS bytes per tile row
     constexpr int CPR = BK / 8;           // 16-byte chunks per row
     constexpr int RP = 256 / ROWB;        // rows per 256 bytes
@@ -121,19 +136,36 @@ void gemm_tile_kernel(GemmArgs g, TileSched ts, int vec_store) {
     auto enter_tile = [&](int q) {
         int shard, tm, tn;
         decode_tile(ts, tile_of(ts, q), shard, tm, tn);
-        const int64_t m0 = (int64_t)tm * TB, n0 = (int64_t)tn * TB;
-        pa = (const char *)((const __bf16 *)g.A + (int64_t)shard * g.a_shard + m0 * g.lda);
+        const int64_t m0 = (int64_t)tm * TB, n0 = (int64_t)tn * TBN;
+        if (XG) {
+            const int64_t sl = m0 / ex.x_rows;
+            pa = (const char *)((const __bf16 *)ex.x_slice[sl] + (int64_t)shard * g.a_shard +
+                                (m0 - sl * ex.x_rows) * g.lda);
+        } else {
+            pa = (const char *)((const __bf16 *)g.A + (int64_t)shard * g.a_shard + m0 * g.lda);
+        }
         pb = (const char *)((const __bf16 *)g.B + (int64_t)shard * g.b_shard + n0 * g.ldb);
         const int a_rows = (int)min<int64_t>(g.M - m0, TB);
-        const int b_rows = (int)min<int64_t>(g.N - n0, TB);
+        const int b_rows = (int)min<int64_t>(g.N - n0, TBN);
 #pragma unroll
         for (int j = 0; j < LPW; ++j) {
             const int r = (j * 4 + wave) * RPI + lane / CPR;
             const int chunk = (lane % CPR) ^ ((r / RP) % CPR);
             const int ra = r < a_rows ? r : a_rows - 1;
-            const int rb = r < b_rows ? r : b_rows - 1;
+            int64_t wrow;
+            if (SWIGLU) {
+                // LDS row r feeds wave r / 128, MFMA block (r / 32) % 4:
+                // blocks 0-1 gate rows, blocks 2-3 the up rows of the same
+                // 64 hidden units.
+                const int blk = (r >> 5) & 3;
+                int h = ((r >> 7) << 6) + ((blk & 1) << 5) + (r & 31);
+                h = h < b_rows ? h : b_rows - 1;
+                wrow = h + (blk >= 2 ? ex.up_off : 0);
+            } else {
+                wrow = r < b_rows ? r : b_rows - 1;
+            }
             aoff[j] = (uint32_t)(((int64_t)ra * g.lda + chunk * 8) * 2);
-            boff[j] = (uint32_t)(((int64_t)rb * g.ldb + chunk * 8) * 2);
+            boff[j] = (uint32_t)((wrow * g.ldb + chunk * 8) * 2);
         }
     };
     // Issue loads [j0, j1) of the cursor's step into `stage` (branch-free;
@@ -304,107 +336,208 @@ void gemm_tile_kernel(GemmArgs g, TileSched ts, int vec_store) {
         // n = 8*r4 + 4*(lane/32) + 0..3 in registers 4*r4..4*r4+3.
         int shard, tm, tn;
         decode_tile(ts, tile_of(ts, q), shard, tm, tn);
-        const int64_t tm0 = (int64_t)tm * TB, tn0 = (int64_t)tn * TB;
+        const int64_t tm0 = (int64_t)tm * TB, tn0 = (int64_t)tn * TBN;
         const int64_t cbase = (int64_t)shard * g.c_shard;
-        // Each 32x32 block goes through this wave's LDS area: written in its
-        // MFMA layout (lane: row m, four consecutive n), read back
-        // row-contiguous, so a store covers whole 64-byte (bf16) or 128-byte
-        // (fp32) row segments.  One path for all tiles: only stores that
-        // cross M or N fall back to element stores.  The stores are
-        // non-temporal: every CU reaches its epilogue at about the same time,
-        // and streaming the burst past L2 keeps it from filling the L2 with
-        // dirty lines the next loads would have to wait behind.
-        {
-            LDS_PTR(char) ep = lds + NST * STAGE + wave * EPI_WAVE;
-            const int64_t tm_w = tm0 + wm * 128, tn_w = tn0 + wn * 128;
-            constexpr int VW = OUT == OUT_BF16 ? 8 : 4;   // values per lane store
-            constexpr int RPP = 64 * VW / 32;              // rows per pass
-            constexpr int ES = OUT == OUT_BF16 ? 2 : 4;    // bytes per value
-            // Tiles inside M x N (all but the last tile row and column) take a
-            // path without per-store bounds tests: one per-lane byte offset
-            // and a uniform base per store.
-            const bool interior = vec_store && tm0 + TB <= g.M && tn0 + TB <= g.N &&
-                                  (int64_t)RPP * g.ldc * ES < (1ll << 31);
-            if (interior) {
-                const uint32_t lane_off =
-                    (uint32_t)(((int64_t)(lane / (32 / VW)) * g.ldc + VW * (lane % (32 / VW))) * ES);
-                char *wbase = (char *)g.C + (cbase + tm_w * g.ldc + tn_w) * ES;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                        for (int r4 = 0; r4 < 4; ++r4) {
-                            const f32x4 v = {acc[i][j][4 * r4], acc[i][j][4 * r4 + 1],
-                                             acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]};
-                            *(LDS_PTR(f32x4))(ep + frow * EPI_ROWB + (8 * r4 + 4 * fhalf) * 4) = v;
-                        }
-#pragma unroll
-                        for (int pp = 0; pp < 32 / RPP; ++pp) {
-                            const int r = pp * RPP + lane / (32 / VW), c = VW * (lane % (32 / VW));
-                            float vv[VW];
-#pragma unroll
-                            for (int h = 0; h < VW / 4; ++h) {
-                                const f32x4 a4 = *(LDS_PTR(f32x4))(ep + r * EPI_ROWB + (c + 4 * h) * 4);
-                                vv[4 * h] = a4[0]; vv[4 * h + 1] = a4[1]; vv[4 * h + 2] = a4[2]; vv[4 * h + 3] = a4[3];
+        if constexpr (EPI == EPI_NONE) {
+            // Each 32x32 block goes through this wave's LDS area: written in its
+            // MFMA layout (lane: row m, four consecutive n), read back
+            // row-contiguous, so a store covers whole 64-byte (bf16) or 128-byte
+            // (fp32) row segments.  One path for all tiles: only stores that
+            // cross M or N fall back to element stores.  The stores are
+            // non-temporal: every CU reaches its epilogue at about the same time,
+            // and streaming the burst past L2 keeps it from filling the L2 with
+            // dirty lines the next loads would have to wait behind.
+            {
+                LDS_PTR(char) ep = lds + NST * STAGE + wave * EPI_WAVE;
+                const int64_t tm_w = tm0 + wm * 128, tn_w = tn0 + wn * 128;
+                constexpr int VW = OUT == OUT_BF16 ? 8 : 4;   // values per lane store
+                constexpr int RPP = 64 * VW / 32;              // rows per pass
+                constexpr int ES = OUT == OUT_BF16 ? 2 : 4;    // bytes per value
+                // Tiles inside M x N (all but the last tile row and column) take a
+                // path without per-store bounds tests: one per-lane byte offset
+                // and a uniform base per store.
+                const bool interior = vec_store && tm0 + TB <= g.M && tn0 + TB <= g.N &&
+                                      (int64_t)RPP * g.ldc * ES < (1ll << 31);
+                if (interior) {
+                    const uint32_t lane_off =
+                        (uint32_t)(((int64_t)(lane / (32 / VW)) * g.ldc + VW * (lane % (32 / VW))) * ES);
+                    char *wbase = (char *)g.C + (cbase + tm_w * g.ldc + tn_w) * ES;
+    #pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+    #pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                            for (int r4 = 0; r4 < 4; ++r4) {
+                                const f32x4 v = {acc[i][j][4 * r4], acc[i][j][4 * r4 + 1],
+                                                 acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]};
+                                *(LDS_PTR(f32x4))(ep + frow * EPI_ROWB + (8 * r4 + 4 * fhalf) * 4) = v;
                             }
-                            char *bp = wbase + ((int64_t)(j * 32 + pp * RPP) * g.ldc + i * 32) * ES + lane_off;
-                            if (OUT == OUT_BF16) {
-                                bf16x8 hv;
-#pragma unroll
-                                for (int e = 0; e < 8; ++e) hv[e] = (__bf16)vv[e];
-                                __builtin_nontemporal_store(hv, (bf16x8 *)bp);
-                            } else {
-                                __builtin_nontemporal_store(f32x4{vv[0], vv[1], vv[2], vv[3]}, (f32x4 *)bp);
+    #pragma unroll
+                            for (int pp = 0; pp < 32 / RPP; ++pp) {
+                                const int r = pp * RPP + lane / (32 / VW), c = VW * (lane % (32 / VW));
+                                float vv[VW];
+    #pragma unroll
+                                for (int h = 0; h < VW / 4; ++h) {
+                                    const f32x4 a4 = *(LDS_PTR(f32x4))(ep + r * EPI_ROWB + (c + 4 * h) * 4);
+                                    vv[4 * h] = a4[0]; vv[4 * h + 1] = a4[1]; vv[4 * h + 2] = a4[2]; vv[4 * h + 3] = a4[3];
+                                }
+                                char *bp = wbase + ((int64_t)(j * 32 + pp * RPP) * g.ldc + i * 32) * ES + lane_off;
+                                if (OUT == OUT_BF16) {
+                                    bf16x8 hv;
+    #pragma unroll
+                                    for (int e = 0; e < 8; ++e) hv[e] = (__bf16)vv[e];
+                                    __builtin_nontemporal_store(hv, (bf16x8 *)bp);
+                                } else {
+                                    __builtin_nontemporal_store(f32x4{vv[0], vv[1], vv[2], vv[3]}, (f32x4 *)bp);
+                                }
+                            }
+                        }
+                    }
+                } else {
+    #pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+    #pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                            for (int r4 = 0; r4 < 4; ++r4) {
+                                const f32x4 v = {acc[i][j][4 * r4], acc[i][j][4 * r4 + 1],
+                                                 acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]};
+                                *(LDS_PTR(f32x4))(ep + frow * EPI_ROWB + (8 * r4 + 4 * fhalf) * 4) = v;
+                            }
+                            const int64_t bm = tm_w + j * 32, bn = tn_w + i * 32;
+    #pragma unroll
+                            for (int pp = 0; pp < 32 / RPP; ++pp) {
+                                const int r = pp * RPP + lane / (32 / VW), c = VW * (lane % (32 / VW));
+                                const int64_t m = bm + r, n = bn + c;
+                                float vv[VW];
+    #pragma unroll
+                                for (int h = 0; h < VW / 4; ++h) {
+                                    const f32x4 a4 = *(LDS_PTR(f32x4))(ep + r * EPI_ROWB + (c + 4 * h) * 4);
+                                    vv[4 * h] = a4[0]; vv[4 * h + 1] = a4[1]; vv[4 * h + 2] = a4[2]; vv[4 * h + 3] = a4[3];
+                                }
+                                if (m < g.M) {
+                                    const int64_t o = cbase + m * g.ldc + n;
+                                    if (vec_store && n + VW <= g.N) {
+                                        if (OUT == OUT_BF16) {
+                                            bf16x8 hv;
+    #pragma unroll
+                                            for (int e = 0; e < 8; ++e) hv[e] = (__bf16)vv[e];
+                                            __builtin_nontemporal_store(hv, (bf16x8 *)((__bf16 *)g.C + o));
+                                        } else {
+                                            __builtin_nontemporal_store(f32x4{vv[0], vv[1], vv[2], vv[3]},
+                                                                        (f32x4 *)((float *)g.C + o));
+                                        }
+                                    } else {
+    #pragma unroll
+                                        for (int e = 0; e < VW; ++e) {
+                                            if (n + e < g.N) {
+                                                if (OUT == OUT_BF16) ((__bf16 *)g.C)[o + e] = (__bf16)vv[e];
+                                                else ((float *)g.C)[o + e] = vv[e];
+                                            }
+                                        }
+                                    }
+                                }
                             }
                         }
                     }
                 }
-            } else {
+            }
+        } else {
+            // With a bias or the gated unit (bf16 output): each 32x32 block
+            // is staged through LDS as above and read back row-contiguous, a
+            // lane holding 8 consecutive columns of a row; the bias and the
+            // activation are applied there, in VGPRs.  For the gated unit the
+            // gate block and then its up block go through the staging area,
+            // so both values of an output meet in the same lane.
+            static_assert(OUT == OUT_BF16, "epilogue options write bf16");
+            LDS_PTR(char) ep = lds + NST * STAGE + wave * EPI_WAVE;
+            constexpr int NI = SWIGLU ? 2 : 4;      // output column blocks per wave
+            constexpr int NH = SWIGLU ? 2 : 1;      // bias vectors per block (gate, up)
+            const int64_t tm_w = tm0 + wm * 128, tn_w = tn0 + wn * (TBN / 2);
+            const int lr = lane >> 2, lc = 8 * (lane & 3);  // row within a 16-row pass, first column
+            const bool has_bias = ex.bias != nullptr;
+            bf16x8 bvec[NI][NH];
+            if (has_bias) {
+                const __bf16 *bb = (const __bf16 *)ex.bias + (int64_t)shard * ex.bias_shard;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int i = 0; i < NI; ++i) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        __builtin_amdgcn_sched_barrier(0);
+                    for (int h = 0; h < NH; ++h) {
+                        const int64_t c = tn_w + i * 32 + lc;
+                        const __bf16 *src = bb + (h ? ex.up_off : 0) + c;
+                        if (c + 7 < g.N) {
+                            bvec[i][h] = *(const bf16x8 *)src;
+                        } else {
 #pragma unroll
-                        for (int r4 = 0; r4 < 4; ++r4) {
-                            const f32x4 v = {acc[i][j][4 * r4], acc[i][j][4 * r4 + 1],
-                                             acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]};
-                            *(LDS_PTR(f32x4))(ep + frow * EPI_ROWB + (8 * r4 + 4 * fhalf) * 4) = v;
+                            for (int e = 0; e < 8; ++e) bvec[i][h][e] = c + e < g.N ? src[e] : (__bf16)0.0f;
                         }
-                        const int64_t bm = tm_w + j * 32, bn = tn_w + i * 32;
+                    }
+                }
+            }
+            auto stage = [&](const f32x16 &a) __attribute__((always_inline)) {
 #pragma unroll
-                        for (int pp = 0; pp < 32 / RPP; ++pp) {
-                            const int r = pp * RPP + lane / (32 / VW), c = VW * (lane % (32 / VW));
-                            const int64_t m = bm + r, n = bn + c;
-                            float vv[VW];
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const f32x4 v = {a[4 * r4], a[4 * r4 + 1], a[4 * r4 + 2], a[4 * r4 + 3]};
+                    *(LDS_PTR(f32x4))(ep + frow * EPI_ROWB + (8 * r4 + 4 * fhalf) * 4) = v;
+                }
+            };
+            auto readback = [&](float (&v)[2][8]) __attribute__((always_inline)) {
 #pragma unroll
-                            for (int h = 0; h < VW / 4; ++h) {
-                                const f32x4 a4 = *(LDS_PTR(f32x4))(ep + r * EPI_ROWB + (c + 4 * h) * 4);
-                                vv[4 * h] = a4[0]; vv[4 * h + 1] = a4[1]; vv[4 * h + 2] = a4[2]; vv[4 * h + 3] = a4[3];
-                            }
-                            if (m < g.M) {
-                                const int64_t o = cbase + m * g.ldc + n;
-                                if (vec_store && n + VW <= g.N) {
-                                    if (OUT == OUT_BF16) {
-                                        bf16x8 hv;
+                for (int pp = 0; pp < 2; ++pp) {
+                    LDS_PTR(char) rp = ep + (pp * 16 + lr) * EPI_ROWB + lc * 4;
+                    const f32x4 a0 = *(LDS_PTR(f32x4))rp, a1 = *(LDS_PTR(f32x4))(rp + 16);
 #pragma unroll
-                                        for (int e = 0; e < 8; ++e) hv[e] = (__bf16)vv[e];
-                                        __builtin_nontemporal_store(hv, (bf16x8 *)((__bf16 *)g.C + o));
-                                    } else {
-                                        __builtin_nontemporal_store(f32x4{vv[0], vv[1], vv[2], vv[3]},
-                                                                    (f32x4 *)((float *)g.C + o));
-                                    }
-                                } else {
+                    for (int e = 0; e < 4; ++e) { v[pp][e] = a0[e]; v[pp][4 + e] = a1[e]; }
+                }
+            };
+            const bool interior = vec_store && tm0 + TB <= g.M && tn0 + TBN <= g.N;
 #pragma unroll
-                                    for (int e = 0; e < VW; ++e) {
-                                        if (n + e < g.N) {
-                                            if (OUT == OUT_BF16) ((__bf16 *)g.C)[o + e] = (__bf16)vv[e];
-                                            else ((float *)g.C)[o + e] = vv[e];
-                                        }
-                                    }
+            for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                for (int i = 0; i < NI; ++i) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    float v[2][8];
+                    stage(acc[i][j]);
+                    readback(v);
+                    if (SWIGLU) {
+                        float u[2][8];
+                        stage(acc[i + 2][j]);
+                        readback(u);
+#pragma unroll
+                        for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) {
+                                float gv = v[pp][e], uv = u[pp][e];
+                                if (has_bias) {
+                                    gv = gv + (float)bvec[i][0][e];
+                                    uv = uv + (float)bvec[i][NH - 1][e];
                                 }
+                                v[pp][e] = silu_f32(gv) * uv;
+                            }
+                    } else if (has_bias) {
+#pragma unroll
+                        for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) v[pp][e] = v[pp][e] + (float)bvec[i][0][e];
+                    }
+#pragma unroll
+                    for (int pp = 0; pp < 2; ++pp) {
+                        const int64_t m = tm_w + j * 32 + pp * 16 + lr, n = tn_w + i * 32 + lc;
+                        bf16x8 hv;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) hv[e] = (__bf16)v[pp][e];
+                        __bf16 *dst = (__bf16 *)g.C + cbase + m * g.ldc + n;
+                        if (interior) {
+                            __builtin_nontemporal_store(hv, (bf16x8 *)dst);
+                        } else if (m < g.M) {
+                            if (vec_store && n + 8 <= g.N) {
+                                __builtin_nontemporal_store(hv, (bf16x8 *)dst);
+                            } else {
+#pragma unroll
+                                for (int e = 0; e < 8; ++e)
+                                    if (n + e < g.N) dst[e] = hv[e];
                             }
                         }
                     }
@@ -446,16 +579,46 @@ constexpr int KERNEL_NST = TPL_TILE_NST;
 
 }  // namespace
 
-bool gemm_tile_supported(const GemmArgs &g) {
-    // 32-bit per-lane offsets: one tile's rows must span < 2 GiB.
-    const bool small_rows = (int64_t)TB * (g.lda > g.ldb ? g.lda : g.ldb) * 2 < (1ll << 31);
-    return g.K > 0 && g.K % KERNEL_BK == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 && g.a_shard % 8 == 0 &&
-           g.b_shard % 8 == 0 && aligned16(g.A) && aligned16(g.B) && small_rows;
+bool gemm_tile_supported(const GemmArgs &g, const GemmExtra *ex) {
+    // 32-bit per-lane offsets: one tile's rows must span < 2 GiB (for the
+    // gated unit, up to the up rows of the tile).
+    const int64_t wspan = TB + (ex && ex->act == ACT_SWIGLU ? ex->up_off : 0);
+    const bool small_rows = (int64_t)TB * g.lda * 2 < (1ll << 31) &&
+                            wspan * g.ldb * 2 < (1ll << 31);
+    bool ok = g.K > 0 && g.K % KERNEL_BK == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 &&
+              g.a_shard % 8 == 0 && g.b_shard % 8 == 0 && aligned16(g.B) && small_rows;
+    if (!ex) return ok && aligned16(g.A);
+    // Bias: 16-byte loads of 8 values per lane.
+    if (ex->bias && (((uintptr_t)ex->bias % 16) != 0 || ex->bias_shard % 8 != 0)) return false;
+    if (ex->act == ACT_SWIGLU && ex->up_off % 8 != 0) return false;
+    if (ex->x_rows > 0) {
+        if (ex->x_rows % TB != 0) return false;
+        const int64_t ns = (g.M + ex->x_rows - 1) / ex->x_rows;
+        for (int64_t j = 0; j < ns; ++j)
+            if (!aligned16(ex->x_slice[j])) return false;
+        return ok;
+    }
+    return ok && aligned16(g.A);
 }
 
-hipError_t launch_gemm_tile(const GemmArgs &g, int out_type, hipStream_t s) {
+namespace {
+
+template <int OUT, int EPI, bool XG>
+hipError_t launch_tile_t(const GemmArgs &g, const TileSched &ts, int vec, const GemmExtra &ex,
+                         int grid, hipStream_t s) {
+    gemm_tile_kernel<KERNEL_BK, KERNEL_NST, OUT, EPI, XG><<<dim3(grid), dim3(TT), 0, s>>>(g, ts, vec, ex);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_tile(const GemmArgs &g, int out_type, const GemmExtra *exp, hipStream_t s) {
     if (g.M == 0 || g.N == 0 || g.P == 0) return hipSuccess;
-    const int64_t tm = (g.M + TB - 1) / TB, tn = (g.N + TB - 1) / TB;
+    GemmExtra ex{};
+    if (exp) ex = *exp;
+    const bool swiglu = ex.act == ACT_SWIGLU;
+    const int tbn = swiglu ? TB / 2 : TB;
+    const int64_t tm = (g.M + TB - 1) / TB, tn = (g.N + tbn - 1) / tbn;
     const int64_t T = tm * tn * g.P;
     if (T > 0x7FFFFFFFll) return hipErrorInvalidConfiguration;
     TileSched ts;
@@ -470,12 +633,21 @@ hipError_t launch_gemm_tile(const GemmArgs &g, int out_type, hipStream_t s) {
     // must keep that alignment.
     const int vw = out_type == OUT_BF16 ? 8 : 4;
     const int vec = (g.ldc % vw == 0) && (g.c_shard % vw == 0) && (((uintptr_t)g.C) % 16 == 0);
-    dim3 block(TT);
-    if (out_type == OUT_BF16)
-        gemm_tile_kernel<KERNEL_BK, KERNEL_NST, OUT_BF16><<<dim3(grid), block, 0, s>>>(g, ts, vec);
-    else
-        gemm_tile_kernel<KERNEL_BK, KERNEL_NST, OUT_F32><<<dim3(grid), block, 0, s>>>(g, ts, vec);
-    return hipGetLastError();
+    const bool xg = ex.x_rows > 0;
+    if (out_type != OUT_BF16) {
+        // fp32 output (row partials): no epilogue options.
+        if (xg || swiglu || ex.bias) return hipErrorInvalidValue;
+        return launch_tile_t<OUT_F32, EPI_NONE, false>(g, ts, vec, ex, grid, s);
+    }
+    const int epi = swiglu ? EPI_SWIGLU : ex.bias ? EPI_BIAS : EPI_NONE;
+    if (xg) {
+        if (epi == EPI_SWIGLU) return launch_tile_t<OUT_BF16, EPI_SWIGLU, true>(g, ts, vec, ex, grid, s);
+        if (epi == EPI_BIAS) return launch_tile_t<OUT_BF16, EPI_BIAS, true>(g, ts, vec, ex, grid, s);
+        return launch_tile_t<OUT_BF16, EPI_NONE, true>(g, ts, vec, ex, grid, s);
+    }
+    if (epi == EPI_SWIGLU) return launch_tile_t<OUT_BF16, EPI_SWIGLU, false>(g, ts, vec, ex, grid, s);
+    if (epi == EPI_BIAS) return launch_tile_t<OUT_BF16, EPI_BIAS, false>(g, ts, vec, ex, grid, s);
+    return launch_tile_t<OUT_BF16, EPI_NONE, false>(g, ts, vec, ex, grid, s);
 }
 
 }  // namespace tpl

@@ -22,6 +22,31 @@ struct GemmArgs {
 };
 
 enum InType { IN_F32 = 0, IN_BF16 = 1 };
+
+constexpr int MAX_SLICES = 64;  // = TP_MAX_SHARDS
+
+// What a column GEMM does besides C_i = A_i B_i^T (all optional).
+//   bias:  per output feature, of the output type; shard i's bias starts at
+//          bias + i*bias_shard (elements).  Added in fp32 before rounding.
+//   swiglu: the gated unit.  Output column c of shard i is
+//          silu(g + bg) * (u + bu) with g from B row c and u from B row
+//          up_off + c of the shard (and the bias at the same offsets), so
+//          g.N counts output columns, not B rows.
+//   x_rows: > 0 when A is given as token slices: row m of A is row
+//          m % x_rows of slice m / x_rows, at x_slice[m / x_rows] with row
+//          stride lda (a_shard then only offsets the column).
+enum ActType { ACT_NONE = 0, ACT_SWIGLU = 1 };
+struct GemmExtra {
+    const void *bias; int64_t bias_shard;
+    int32_t act; int64_t up_off;
+    int64_t x_rows;
+    const void *x_slice[MAX_SLICES];
+};
+
+// silu(v) = v * sigmoid(v) = v / (1 + e^-v), fp32, shared by every kernel
+// that applies the gated unit.  For v below about -88 the exponential is
+// +inf and the quotient a signed zero, the function's limit.
+__device__ __forceinline__ float silu_f32(float v) { return v / (1.0f + __expf(-v)); }
 enum OutType { OUT_F32 = 0, OUT_BF16 = 1 };
 
 // Fused fold for the skinny row GEMM: each workgroup walks all P shards of
@@ -32,31 +57,53 @@ struct FoldArgs {
 };
 
 // 256x256x64 bf16 MFMA tile kernel.  Requires K > 0, K % 64 == 0, lda, ldb,
-// a_shard, b_shard multiples of 8 and A, B 16-byte aligned.
-hipError_t launch_gemm_tile(const GemmArgs &g, int out_type, hipStream_t s);
-bool gemm_tile_supported(const GemmArgs &g);
+// a_shard, b_shard multiples of 8 and A, B 16-byte aligned; with x slices,
+// x_rows a multiple of 256 and every slice 16-byte aligned.
+hipError_t launch_gemm_tile(const GemmArgs &g, int out_type, const GemmExtra *ex,
+                            hipStream_t s);
+bool gemm_tile_supported(const GemmArgs &g, const GemmExtra *ex);
 
 // Skinny (M <= 64) bf16 kernel that streams W.  Requires K > 0, K % 8 == 0,
 // lda, ldb, a_shard, b_shard multiples of 8 and A, B 16-byte aligned.
 // fold == nullptr: C_i written as out_type.  fold != nullptr: C is unused
 // and the fold of the P shard products is written to fold->Y.
+// ex: bias and the gated unit (column form), or the bias added after the
+// fold (fused form); x slices are not taken here.
 hipError_t launch_gemm_skinny(const GemmArgs &g, int out_type, const FoldArgs *fold,
-                              hipStream_t s);
-bool gemm_skinny_supported(const GemmArgs &g);
+                              const GemmExtra *ex, hipStream_t s);
+bool gemm_skinny_supported(const GemmArgs &g, const GemmExtra *ex);
 constexpr int SKINNY_MAX_M = 64;
 
-// Any shape, stride or alignment; fp32 or bf16 inputs.
-hipError_t launch_gemm_generic(const GemmArgs &g, int in_type, int out_type, hipStream_t s);
+// Any shape, stride or alignment; fp32 or bf16 inputs; every GemmExtra option.
+hipError_t launch_gemm_generic(const GemmArgs &g, int in_type, int out_type,
+                               const GemmExtra *ex, hipStream_t s);
 
 // Ascending-shard fold of P fp32 parts into Y (optionally scattered into
 // token slices: output row m goes to slice m / slice_rows at
 // Y + (m / slice_rows)*slice_stride + (m % slice_rows)*ldy).
+// With use_slices, slice j is at y_slice[j] instead (slice_stride unused).
+// bias (optional, of the output type, [N]) is added once after the fold.
 struct ReduceArgs {
     const float *partials; int64_t shard_stride; int64_t ldp;
     void *Y; int64_t ldy; int64_t slice_rows; int64_t slice_stride;
     int64_t M, N; int32_t P;
+    const void *bias;
+    int32_t use_slices;
+    void *y_slice[MAX_SLICES];
 };
 hipError_t launch_shard_fold(const ReduceArgs &r, int out_type, hipStream_t s);
+
+// Feature-sharded embedding lookup: for token t and shard i,
+//   Y row t, columns [i*Ds, (i+1)*Ds)  (CONCAT), or block i row t (SHARDS)
+//   = row ids[t] of shard i (e_shard[i], row stride lde), Ds = D / P;
+// an id outside [0, V) writes zeros and sets *bad to 1 when bad != nullptr.
+struct EmbedArgs {
+    const int64_t *ids; int64_t T, V, Ds; int32_t P;
+    int64_t lde; void *Y; int64_t ldy; int64_t y_shard;
+    int32_t *bad;
+    const void *e_shard[MAX_SLICES];
+};
+hipError_t launch_embedding(const EmbedArgs &e, int elem_bytes, hipStream_t s);
 
 hipError_t launch_fill_zero(void *ptr, size_t words, hipStream_t s);
 

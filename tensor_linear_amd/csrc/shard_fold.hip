@@ -13,6 +13,11 @@
 // code, not by scheduling.  (Measured on 8 partials of 4096 x 4096 and of
 // 16384 x 8192: 5-12% faster than 8 lane-contiguous columns per lane, whose
 // loads each cover a 2 KB span at half density.)
+//
+// The row bias is Partial() ("Module 并行：实现 DP/TP/CP/PP 组合", "Linear
+// 实现解析"): its parts sum to the layer's bias, so it is added once, after
+// the last shard, before the rounding.  The token slices may also sit in P
+// separate allocations (a pointer per slice), as P ranks would hold them.
 #include "kernels.h"
 
 namespace tpl {
@@ -26,9 +31,19 @@ constexpr int FOLD_BATCH = 8;  // shards loaded before their adds are issued
 constexpr int FOLD_G = 4;      // 4-column groups per lane
 constexpr int FOLD_WCOLS = 64 * 4 * FOLD_G;  // columns per wavefront
 
-__device__ __forceinline__ int64_t out_offset(const ReduceArgs &r, int64_t m, int64_t n) {
+// Element pointer of output (m, n) (element size ES).
+template <int ES>
+__device__ __forceinline__ char *out_ptr(const ReduceArgs &r, int64_t m, int64_t n) {
     const int64_t j = m / r.slice_rows;
-    return j * r.slice_stride + (m - j * r.slice_rows) * r.ldy + n;
+    const int64_t row = m - j * r.slice_rows;
+    if (r.use_slices) return (char *)r.y_slice[j] + (row * r.ldy + n) * ES;
+    return (char *)r.Y + (j * r.slice_stride + row * r.ldy + n) * ES;
+}
+
+template <int OUT>
+__device__ __forceinline__ float bias_at(const void *b, int64_t n) {
+    if (OUT == OUT_BF16) return (float)((const __bf16 *)b)[n];
+    return ((const float *)b)[n];
 }
 
 template <int OUT>
@@ -71,17 +86,32 @@ void shard_fold_vec(ReduceArgs r) {
             }
         }
     }
+    if (r.bias) {
+#pragma unroll
+        for (int h = 0; h < FOLD_G; ++h) {
+            if (!in[h]) continue;
+            const int64_t n = nw + h * 256 + 4 * lane;
+            f32x4 b;
+            if (OUT == OUT_BF16) {
+                const bf16x4 bv = *(const bf16x4 *)((const __bf16 *)r.bias + n);
+                b = f32x4{(float)bv[0], (float)bv[1], (float)bv[2], (float)bv[3]};
+            } else {
+                b = *(const f32x4 *)((const float *)r.bias + n);
+            }
+            a[h] = a[h] + b;
+        }
+    }
 #pragma unroll
     for (int h = 0; h < FOLD_G; ++h) {
         if (!in[h]) continue;
-        const int64_t o = out_offset(r, m, nw + h * 256 + 4 * lane);
+        const int64_t n = nw + h * 256 + 4 * lane;
         if (OUT == OUT_BF16) {
             bf16x4 hv;
             hv[0] = (__bf16)a[h][0]; hv[1] = (__bf16)a[h][1];
             hv[2] = (__bf16)a[h][2]; hv[3] = (__bf16)a[h][3];
-            __builtin_nontemporal_store(hv, (bf16x4 *)((__bf16 *)r.Y + o));
+            __builtin_nontemporal_store(hv, (bf16x4 *)out_ptr<2>(r, m, n));
         } else {
-            __builtin_nontemporal_store(a[h], (f32x4 *)((float *)r.Y + o));
+            __builtin_nontemporal_store(a[h], (f32x4 *)out_ptr<4>(r, m, n));
         }
     }
 }
@@ -96,11 +126,11 @@ void shard_fold_scalar(ReduceArgs r) {
     const float *p = r.partials + m * r.ldp + n;
     float a = p[0];
     for (int i = 1; i < r.P; ++i) a = a + p[(int64_t)i * r.shard_stride];
-    const int64_t o = out_offset(r, m, n);
+    if (r.bias) a = a + bias_at<OUT>(r.bias, n);
     if (OUT == OUT_BF16)
-        ((__bf16 *)r.Y)[o] = (__bf16)a;
+        *(__bf16 *)out_ptr<2>(r, m, n) = (__bf16)a;
     else
-        ((float *)r.Y)[o] = a;
+        *(float *)out_ptr<4>(r, m, n) = a;
 }
 
 __global__ __launch_bounds__(256)
@@ -118,10 +148,18 @@ hipError_t launch_shard_fold(const ReduceArgs &r, int out_type, hipStream_t s) {
     if (r.M == 0 || r.N == 0) return hipSuccess;
     // Vector path: 16-byte partial loads and 4-value stores (8 bytes bf16,
     // 16 bytes fp32), so rows, shards and output slices keep that alignment.
-    const bool y_ok = out_type == OUT_BF16 ? ((uintptr_t)r.Y % 8 == 0) : aligned16(r.Y);
+    auto out_ok = [&](const void *p) {
+        return out_type == OUT_BF16 ? ((uintptr_t)p % 8 == 0) : aligned16(p);
+    };
+    bool y_ok = true;
+    if (r.use_slices) {
+        for (int64_t j = 0; j * r.slice_rows < r.M; ++j) y_ok = y_ok && out_ok(r.y_slice[j]);
+    } else {
+        y_ok = out_ok(r.Y) && (r.slice_stride % 4 == 0);
+    }
+    const bool b_ok = !r.bias || out_ok(r.bias);
     const bool vec = (r.N % 4 == 0) && (r.ldp % 4 == 0) && (r.shard_stride % 4 == 0) &&
-                     aligned16(r.partials) && y_ok && (r.ldy % 4 == 0) &&
-                     (r.slice_stride % 4 == 0);
+                     aligned16(r.partials) && y_ok && b_ok && (r.ldy % 4 == 0);
     const int64_t work = vec ? r.M * ((r.N + FOLD_WCOLS - 1) / FOLD_WCOLS) * 64 : r.M * r.N;
     const int64_t blocks = (work + FOLD_THREADS - 1) / FOLD_THREADS;
     if (blocks > 0x7FFFFFFFll) return hipErrorInvalidConfiguration;

@@ -32,13 +32,22 @@ tp_status check_gemm_shape(int64_t M, int64_t N, int64_t K, int32_t P, int64_t l
 // Decode-shaped bf16 problems (M <= 64) stream W with the skinny kernel;
 // large aligned bf16 problems use the 256x256 MFMA tile kernel; everything
 // else (fp32, odd K, unaligned views) uses the generic kernel.
-hipError_t run_gemm(const GemmArgs &g, int32_t dtype, int out_type, hipStream_t s) {
+hipError_t run_gemm(const GemmArgs &g, int32_t dtype, int out_type, const GemmExtra *ex,
+                    hipStream_t s) {
     if (dtype == TP_BF16) {
-        if (gemm_skinny_supported(g)) return launch_gemm_skinny(g, out_type, nullptr, s);
-        if (gemm_tile_supported(g)) return launch_gemm_tile(g, out_type, s);
-        return launch_gemm_generic(g, IN_BF16, out_type, s);
+        if (gemm_skinny_supported(g, ex)) return launch_gemm_skinny(g, out_type, nullptr, ex, s);
+        if (gemm_tile_supported(g, ex)) return launch_gemm_tile(g, out_type, ex, s);
+        return launch_gemm_generic(g, IN_BF16, out_type, ex, s);
     }
-    return launch_gemm_generic(g, IN_F32, out_type, s);
+    return launch_gemm_generic(g, IN_F32, out_type, ex, s);
+}
+
+inline size_t dtype_bytes(int32_t d) { return d == TP_BF16 ? 2 : 4; }
+
+// Fill the slice table of r from a host array (nullptr: the strided layout).
+void set_out_slices(ReduceArgs &r, void *const *y_slices, int32_t P) {
+    r.use_slices = y_slices ? 1 : 0;
+    for (int j = 0; j < MAX_SLICES; ++j) r.y_slice[j] = (y_slices && j < P) ? y_slices[j] : nullptr;
 }
 
 size_t partials_bytes(int64_t M, int64_t N, int32_t P) {
@@ -102,27 +111,56 @@ tp_status tp_shard_layout(int64_t rows, int64_t cols, int64_t ld, tp_placement p
     return TP_ERR_PLACEMENT;
 }
 
-tp_status tp_linear_column(const void *X, int64_t ldx, const void *W, int64_t ldw, void *Y,
-                           int64_t ldy, int32_t y_mode, int64_t M, int64_t N, int64_t K,
-                           int32_t P, int32_t dtype, void *stream) {
+tp_status tp_linear_column_ex(const void *X, const void *const *x_slices, int64_t ldx,
+                              const void *W, int64_t ldw, const void *bias, void *Y, int64_t ldy,
+                              int32_t y_mode, int32_t act, int64_t M, int64_t N, int64_t K,
+                              int32_t P, int32_t dtype, void *stream) {
     tp_status st = check_gemm_shape(M, N, K, P, ldx, ldw);
     if (st != TP_OK) return st;
     if (!valid_dtype(dtype)) return TP_ERR_DTYPE;
     if (y_mode != TP_Y_CONCAT && y_mode != TP_Y_SHARDS) return TP_ERR_MODE;
+    if (act != TP_ACT_NONE && act != TP_ACT_SWIGLU) return TP_ERR_MODE;
     if (N % P != 0) return TP_ERR_INDIVISIBLE;
-    const int64_t Ns = N / P;
-    if (y_mode == TP_Y_CONCAT ? ldy < N : ldy < Ns) return TP_ERR_SHAPE;
+    const int64_t Ns = N / P;                                   // W rows per shard
+    const bool swiglu = act == TP_ACT_SWIGLU;
+    if (swiglu && Ns % 2 != 0) return TP_ERR_INDIVISIBLE;
+    const int64_t On = swiglu ? Ns / 2 : Ns;                     // outputs per shard
+    if (x_slices && M % P != 0) return TP_ERR_INDIVISIBLE;
+    if (y_mode == TP_Y_CONCAT ? ldy < On * P : ldy < On) return TP_ERR_SHAPE;
     if (ldy < 1) return TP_ERR_SHAPE;
     if (M == 0 || N == 0) return TP_OK;
-    if (!Y || (K > 0 && (!X || !W))) return TP_ERR_NULL;
+    if (!Y) return TP_ERR_NULL;
+    if (K > 0) {
+        if (!W || (X != nullptr) == (x_slices != nullptr)) return TP_ERR_NULL;
+        if (x_slices)
+            for (int32_t j = 0; j < P; ++j)
+                if (!x_slices[j]) return TP_ERR_NULL;
+    }
 
     GemmArgs g;
     g.A = X; g.lda = ldx; g.a_shard = 0;
     g.B = W; g.ldb = ldw; g.b_shard = Ns * ldw;
-    g.C = Y; g.ldc = ldy; g.c_shard = y_mode == TP_Y_CONCAT ? Ns : M * ldy;
-    g.M = M; g.N = Ns; g.K = K; g.P = P;
+    g.C = Y; g.ldc = ldy; g.c_shard = y_mode == TP_Y_CONCAT ? On : M * ldy;
+    g.M = M; g.N = On; g.K = K; g.P = P;
+    GemmExtra ex{};
+    ex.bias = bias; ex.bias_shard = Ns;
+    ex.act = swiglu ? ACT_SWIGLU : ACT_NONE; ex.up_off = swiglu ? On : 0;
+    ex.x_rows = 0;
+    if (x_slices && K > 0) {
+        ex.x_rows = M / P;
+        for (int32_t j = 0; j < P; ++j) ex.x_slice[j] = x_slices[j];
+        g.A = x_slices[0];
+    }
+    const bool plain = !bias && !swiglu && ex.x_rows == 0;
     const int out = dtype == TP_BF16 ? OUT_BF16 : OUT_F32;
-    return hip_status(run_gemm(g, dtype, out, (hipStream_t)stream));
+    return hip_status(run_gemm(g, dtype, out, plain ? nullptr : &ex, (hipStream_t)stream));
+}
+
+tp_status tp_linear_column(const void *X, int64_t ldx, const void *W, int64_t ldw, void *Y,
+                           int64_t ldy, int32_t y_mode, int64_t M, int64_t N, int64_t K,
+                           int32_t P, int32_t dtype, void *stream) {
+    return tp_linear_column_ex(X, nullptr, ldx, W, ldw, nullptr, Y, ldy, y_mode, TP_ACT_NONE,
+                               M, N, K, P, dtype, stream);
 }
 
 size_t tp_row_workspace_bytes(int32_t mode, int64_t M, int64_t N, int32_t P) {
@@ -135,20 +173,29 @@ size_t tp_row_workspace_bytes(int32_t mode, int64_t M, int64_t N, int32_t P) {
     }
 }
 
-tp_status tp_linear_row(const void *X, int64_t ldx, const void *W, int64_t ldw, void *Y,
-                        int64_t ldy, int64_t y_slice_stride, int32_t mode, void *workspace,
-                        size_t ws_bytes, int64_t M, int64_t N, int64_t K, int32_t P,
-                        int32_t dtype, void *stream) {
+tp_status tp_linear_row_ex(const void *X, int64_t ldx, const void *W, int64_t ldw,
+                           const void *bias, void *Y, void *const *y_slices, int64_t ldy,
+                           int64_t y_slice_stride, int32_t mode, void *workspace,
+                           size_t ws_bytes, int64_t M, int64_t N, int64_t K, int32_t P,
+                           int32_t dtype, void *stream) {
     tp_status st = check_gemm_shape(M, N, K, P, ldx, ldw);
     if (st != TP_OK) return st;
     if (!valid_dtype(dtype)) return TP_ERR_DTYPE;
     if (mode < TP_ROW_PARTIAL || mode > TP_ROW_SCATTER) return TP_ERR_MODE;
+    if (bias && mode == TP_ROW_PARTIAL) return TP_ERR_MODE;
+    if (y_slices && mode != TP_ROW_SCATTER) return TP_ERR_MODE;
     if (K % P != 0) return TP_ERR_INDIVISIBLE;
     if (mode == TP_ROW_SCATTER && M % P != 0) return TP_ERR_INDIVISIBLE;
     if (ldy < N || ldy < 1) return TP_ERR_SHAPE;
     if (y_slice_stride < 0) return TP_ERR_SHAPE;
     if (M == 0 || N == 0) return TP_OK;
-    if (!Y || (K > 0 && (!X || !W))) return TP_ERR_NULL;
+    if (y_slices) {
+        for (int32_t j = 0; j < P; ++j)
+            if (!y_slices[j]) return TP_ERR_NULL;
+    } else if (!Y) {
+        return TP_ERR_NULL;
+    }
+    if (K > 0 && (!X || !W)) return TP_ERR_NULL;
     const size_t need = tp_row_workspace_bytes(mode, M, N, P);
     if (need > 0 && (!workspace || ws_bytes < need || ((uintptr_t)workspace % WS_ALIGN) != 0))
         return TP_ERR_WORKSPACE;
@@ -163,23 +210,27 @@ tp_status tp_linear_row(const void *X, int64_t ldx, const void *W, int64_t ldw, 
 
     if (mode == TP_ROW_PARTIAL) {
         g.C = Y; g.ldc = ldy; g.c_shard = M * ldy;
-        return hip_status(run_gemm(g, dtype, OUT_F32, s));
+        return hip_status(run_gemm(g, dtype, OUT_F32, nullptr, s));
     }
 
     float *parts = (float *)workspace;
     g.C = parts; g.ldc = N; g.c_shard = M * N;
 
-    if (mode == TP_ROW_FUSED && dtype == TP_BF16 && gemm_skinny_supported(g)) {
+    if (mode == TP_ROW_FUSED && dtype == TP_BF16 && gemm_skinny_supported(g, nullptr)) {
         FoldArgs f;
         f.Y = Y; f.ldy = ldy; f.out_type = out;
-        return hip_status(launch_gemm_skinny(g, out, &f, s));
+        GemmExtra ex{};
+        ex.bias = bias;
+        return hip_status(launch_gemm_skinny(g, out, &f, bias ? &ex : nullptr, s));
     }
 
-    hipError_t e = run_gemm(g, dtype, OUT_F32, s);
+    hipError_t e = run_gemm(g, dtype, OUT_F32, nullptr, s);
     if (e != hipSuccess) return TP_ERR_HIP;
     ReduceArgs r;
     r.partials = parts; r.shard_stride = M * N; r.ldp = N;
     r.Y = Y; r.ldy = ldy; r.M = M; r.N = N; r.P = P;
+    r.bias = bias;
+    set_out_slices(r, y_slices, P);
     if (mode == TP_ROW_SCATTER) {
         r.slice_rows = M / P;
         r.slice_stride = y_slice_stride ? y_slice_stride : (M / P) * ldy;
@@ -190,20 +241,38 @@ tp_status tp_linear_row(const void *X, int64_t ldx, const void *W, int64_t ldw, 
     return hip_status(launch_shard_fold(r, out, s));
 }
 
-tp_status tp_shard_reduce(const float *partials, int64_t shard_stride, int64_t ldp, void *Y,
-                          int64_t ldy, int64_t y_slice_stride, int32_t scatter, int64_t M,
-                          int64_t N, int32_t P, int32_t out_dtype, void *stream) {
+tp_status tp_linear_row(const void *X, int64_t ldx, const void *W, int64_t ldw, void *Y,
+                        int64_t ldy, int64_t y_slice_stride, int32_t mode, void *workspace,
+                        size_t ws_bytes, int64_t M, int64_t N, int64_t K, int32_t P,
+                        int32_t dtype, void *stream) {
+    return tp_linear_row_ex(X, ldx, W, ldw, nullptr, Y, nullptr, ldy, y_slice_stride, mode,
+                            workspace, ws_bytes, M, N, K, P, dtype, stream);
+}
+
+tp_status tp_shard_reduce_ex(const float *partials, int64_t shard_stride, int64_t ldp,
+                             const void *bias, void *Y, void *const *y_slices, int64_t ldy,
+                             int64_t y_slice_stride, int32_t scatter, int64_t M, int64_t N,
+                             int32_t P, int32_t out_dtype, void *stream) {
     if (M < 0 || N < 0 || P < 1 || P > TP_MAX_SHARDS) return TP_ERR_SHAPE;
     if (ldp < N || ldy < N || ldp < 1 || ldy < 1 || shard_stride < 0 || y_slice_stride < 0)
         return TP_ERR_SHAPE;
     if (!valid_dtype(out_dtype)) return TP_ERR_DTYPE;
     if (scatter != 0 && scatter != 1) return TP_ERR_MODE;
+    if (y_slices && !scatter) return TP_ERR_MODE;
     if (scatter && M % P != 0) return TP_ERR_INDIVISIBLE;
     if (M == 0 || N == 0) return TP_OK;
-    if (!partials || !Y) return TP_ERR_NULL;
+    if (!partials) return TP_ERR_NULL;
+    if (y_slices) {
+        for (int32_t j = 0; j < P; ++j)
+            if (!y_slices[j]) return TP_ERR_NULL;
+    } else if (!Y) {
+        return TP_ERR_NULL;
+    }
     ReduceArgs r;
     r.partials = partials; r.shard_stride = shard_stride; r.ldp = ldp;
     r.Y = Y; r.ldy = ldy; r.M = M; r.N = N; r.P = P;
+    r.bias = bias;
+    set_out_slices(r, y_slices, P);
     if (scatter) {
         r.slice_rows = M / P;
         r.slice_stride = y_slice_stride ? y_slice_stride : (M / P) * ldy;
@@ -213,6 +282,45 @@ tp_status tp_shard_reduce(const float *partials, int64_t shard_stride, int64_t l
     }
     return hip_status(launch_shard_fold(r, out_dtype == TP_BF16 ? OUT_BF16 : OUT_F32,
                                         (hipStream_t)stream));
+}
+
+tp_status tp_shard_reduce(const float *partials, int64_t shard_stride, int64_t ldp, void *Y,
+                          int64_t ldy, int64_t y_slice_stride, int32_t scatter, int64_t M,
+                          int64_t N, int32_t P, int32_t out_dtype, void *stream) {
+    return tp_shard_reduce_ex(partials, shard_stride, ldp, nullptr, Y, nullptr, ldy,
+                              y_slice_stride, scatter, M, N, P, out_dtype, stream);
+}
+
+tp_status tp_embedding(const int64_t *ids, int64_t T, const void *E, const void *const *e_shards,
+                       int64_t lde, int64_t V, int64_t D, void *Y, int64_t ldy, int32_t y_mode,
+                       int32_t P, int32_t dtype, int32_t *bad_flag, void *stream) {
+    if (T < 0 || V < 0 || D < 0 || P < 1 || P > TP_MAX_SHARDS) return TP_ERR_SHAPE;
+    if (!valid_dtype(dtype)) return TP_ERR_DTYPE;
+    if (y_mode != TP_Y_CONCAT && y_mode != TP_Y_SHARDS) return TP_ERR_MODE;
+    if (D % P != 0) return TP_ERR_INDIVISIBLE;
+    const int64_t Ds = D / P;
+    if (E ? lde < D : lde < Ds) return TP_ERR_SHAPE;
+    if (lde < 1) return TP_ERR_SHAPE;
+    if (y_mode == TP_Y_CONCAT ? ldy < D : ldy < Ds) return TP_ERR_SHAPE;
+    if (ldy < 1) return TP_ERR_SHAPE;
+    if (T == 0 || D == 0) return TP_OK;
+    if (!ids || !Y || (E != nullptr) == (e_shards != nullptr)) return TP_ERR_NULL;
+    EmbedArgs e;
+    e.ids = ids; e.T = T; e.V = V; e.Ds = Ds; e.P = P;
+    e.lde = lde; e.Y = Y; e.ldy = ldy;
+    e.y_shard = y_mode == TP_Y_CONCAT ? Ds : T * ldy;
+    e.bad = bad_flag;
+    const size_t es = dtype_bytes(dtype);
+    for (int j = 0; j < MAX_SLICES; ++j) e.e_shard[j] = nullptr;
+    for (int32_t i = 0; i < P; ++i) {
+        if (e_shards) {
+            if (!e_shards[i]) return TP_ERR_NULL;
+            e.e_shard[i] = e_shards[i];
+        } else {
+            e.e_shard[i] = (const char *)E + (size_t)i * Ds * es;
+        }
+    }
+    return hip_status(launch_embedding(e, (int)es, (hipStream_t)stream));
 }
 
 tp_status tp_workspace_zero(void *ptr, size_t bytes, void *stream) {
