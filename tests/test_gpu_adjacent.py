@@ -428,3 +428,45 @@ def test_embedding_out_of_range_ids():
     tl.tp_embedding(idd, Y, P, E=Ed, bad=bad)
     assert np.array_equal(bits(Y), oracle.embedding_parallel(ids, Eb, P))
     assert int(bad.item()) == 1
+
+
+# ---------------------------------------------------------------------------
+# Guard cells: the epilogue options write exactly their output view.
+# ---------------------------------------------------------------------------
+
+GUARD = [
+    # (M, K, N, P, act): tile path with whole and ragged tiles, skinny, generic
+    (300, 128, 2 * 272, 2, tl.TP_ACT_NONE),
+    (300, 128, 2 * 272, 2, tl.TP_ACT_SWIGLU),
+    (512, 128, 4 * 256, 4, tl.TP_ACT_SWIGLU),
+    (9, 256, 2 * 48, 2, tl.TP_ACT_SWIGLU),
+    (9, 256, 2 * 48, 2, tl.TP_ACT_NONE),
+    (70, 40, 3 * 12, 3, tl.TP_ACT_SWIGLU),
+]
+
+
+@pytest.mark.parametrize("case", range(len(GUARD)))
+@pytest.mark.parametrize("first_col", [8, 1])
+def test_epilogue_guard_cells(case, first_col):
+    # The output is a view into a wider buffer filled with a sentinel; the view
+    # starts at column `first_col` (8: 16-byte aligned rows, vector stores;
+    # 1: unaligned, element stores).  Every cell outside the view keeps its
+    # bits, and the view equals the call on a dense output.
+    M, K, N, P, act = GUARD[case]
+    print(f"guard M={M} K={K} N={N} P={P} act={act} first_col={first_col}", flush=True)
+    On = N // P // (2 if act == tl.TP_ACT_SWIGLU else 1)
+    X = _dev(_ints(990 + case, (M, K)), torch.bfloat16)
+    W = _dev(_ints(991 + case, (N, K)), torch.bfloat16)
+    b = _dev(_ints(992 + case, (N,), -4, 4), torch.bfloat16)
+    sentinel = -12345.0
+    buf = torch.full((M + 2, On * P + 16), sentinel, dtype=torch.bfloat16, device=DEV)
+    view = buf[1:M + 1, first_col:first_col + On * P]
+    tl.tp_linear_column_ex(X, W, view, P, bias=b, act=act)
+    dense = torch.empty((M, On * P), dtype=torch.bfloat16, device=DEV)
+    tl.tp_linear_column_ex(X, W, dense, P, bias=b, act=act)
+    torch.cuda.synchronize()
+    got = buf.cpu()
+    mask = torch.ones_like(got, dtype=torch.bool)
+    mask[1:M + 1, first_col:first_col + On * P] = False
+    assert torch.all(got[mask] == sentinel), "a cell outside the output view was written"
+    assert torch.equal(view.cpu().view(torch.int16), dense.cpu().view(torch.int16))
