@@ -15,7 +15,8 @@
 // CU sits idle between tiles.  Workgroup b runs on XCD b % 8; the tiles are
 // split into 8 contiguous ranges, one per XCD, and inside a range the 32
 // workgroups of the XCD take consecutive tiles (visited in groups of 8
-// tile-rows), so the panels of X and W they share stay in that XCD's L2.
+// tile-rows, 4 for fp32 partials), so the panels of X and W they share stay
+// in that XCD's L2.
 //
 // Global -> LDS: global_load_lds_dwordx4 (16 bytes per lane straight into
 // LDS, no register staging), NST stages of BK columns of K.  One wave
@@ -56,27 +57,27 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int TB = 256;  // tile edge in M and N (W rows)
 constexpr int TT = 256;  // threads
-constexpr int GROUP_M = 8;
 
 enum { EPI_NONE = 0, EPI_BIAS = 1, EPI_SWIGLU = 2 };
 
 struct TileSched {
     int tiles_m, tiles_n;  // per shard
+    int group_m;           // tile rows visited as a group inside a shard
     int T;                 // tiles over all shards
     int xcd_split;         // 1: XCD-contiguous ranges (grid == 8 * per_xcd)
     int per_xcd;           // workgroups per XCD when xcd_split
 };
 
 // Logical tile index -> (shard, tile row, tile column), tile rows grouped by
-// GROUP_M inside a shard.
+// group_m inside a shard.
 __device__ __forceinline__ void decode_tile(const TileSched &ts, int logical, int &shard,
                                            int &tm, int &tn) {
     const int per_shard = ts.tiles_m * ts.tiles_n;
     shard = logical / per_shard;
     const int t = logical - shard * per_shard;
-    const int in_group = GROUP_M * ts.tiles_n;
-    const int first_m = (t / in_group) * GROUP_M;
-    const int gsz = min(ts.tiles_m - first_m, GROUP_M);
+    const int in_group = ts.group_m * ts.tiles_n;
+    const int first_m = (t / in_group) * ts.group_m;
+    const int gsz = min(ts.tiles_m - first_m, ts.group_m);
     const int tr = t - (t / in_group) * in_group;
     tm = first_m + tr % gsz;
     tn = tr / gsz;
@@ -624,6 +625,10 @@ hipError_t launch_gemm_tile(const GemmArgs &g, int out_type, const GemmExtra *ex
     TileSched ts;
     ts.tiles_m = (int)tm;
     ts.tiles_n = (int)tn;
+    // Groups of 8 tile rows for the bf16 column products, 4 for the fp32
+    // row partials (measured on one box: fc2 +1.2-1.4%, Llama-70B O row
+    // +1.7-2.2% with 4; column products equal or better with 8).
+    ts.group_m = out_type == OUT_BF16 ? 8 : 4;
     ts.T = (int)T;
     const int cus = num_cus();
     int grid = (int)(T < cus ? T : cus);
