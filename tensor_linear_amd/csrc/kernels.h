@@ -93,6 +93,14 @@ struct ReduceArgs {
 };
 hipError_t launch_shard_fold(const ReduceArgs &r, int out_type, hipStream_t s);
 
+// Row GEMM with the fold of the P shard partials in registers (bf16 in and
+// out; 256x128 tiles): writes the fold (+ r.bias) of the products
+// A_i B_i^T, i ascending, where r places the output (Y, ldy, token slices);
+// the partials fields of r are unused.  Same requirements as the tile
+// kernel; for a reduce-scatter, slice_rows a multiple of 256.
+hipError_t launch_gemm_rowfold(const GemmArgs &g, const ReduceArgs &r, hipStream_t s);
+bool gemm_rowfold_supported(const GemmArgs &g, const ReduceArgs &r);
+
 // Feature-sharded embedding lookup: for token t and shard i,
 //   Y row t, columns [i*Ds, (i+1)*Ds)  (CONCAT), or block i row t (SHARDS)
 //   = row ids[t] of shard i (e_shard[i], row stride lde), Ds = D / P;
