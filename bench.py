@@ -254,8 +254,8 @@ def traffic_bytes(wid, op):
     except (OSError, KeyError, ValueError):
         return None
     k = rec["kernel"]
-    files = {"tile": "gemm_tile.hip", "skinny": "gemm_skinny.hip", "fold": "shard_fold.hip",
-             "embedding": "embedding.hip", "generic": "gemm_generic.hip"}
+    files = {"rowfold": "gemm_rowfold.hip", "tile": "gemm_tile.hip", "skinny": "gemm_skinny.hip",
+             "fold": "shard_fold.hip", "embedding": "embedding.hip", "generic": "gemm_generic.hip"}
     srcs = next((f for key, f in files.items() if key in k), None)
     if srcs is None:
         return None
