@@ -22,7 +22,7 @@ LIB = os.path.join(HERE, "libtplinear.so")
 CLOCK_LIB = os.path.join(HERE, "libtplclock.so")
 CLOCK_SOURCE = "clock_probe.hip"
 
-SOURCES = ["tplinear.cpp", "gemm_tile.hip", "gemm_skinny.hip", "gemm_generic.hip",
+SOURCES = ["tplinear.cpp", "device.cpp", "gemm_tile.hip", "gemm_skinny.hip", "gemm_generic.hip",
            "shard_fold.hip", "embedding.hip", "gemm_rowfold.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

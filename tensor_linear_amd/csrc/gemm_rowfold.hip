@@ -332,19 +332,6 @@ void gemm_rowfold_kernel(GemmArgs g, FoldSched ts, ReduceArgs ro, int vec_store)
 
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-int fold_num_cus() {
-    static int n = 0;
-    if (n == 0) {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-            v > 0)
-            n = v;
-        else
-            n = 256;
-    }
-    return n;
-}
 
 }  // namespace
 
@@ -368,7 +355,7 @@ hipError_t launch_gemm_rowfold(const GemmArgs &g, const ReduceArgs &ro, hipStrea
     ts.tiles_m = (int)tm;
     ts.tiles_n = (int)tn;
     ts.T = (int)T;
-    const int cus = fold_num_cus();
+    const int cus = device_cu_count();
     const int grid = (int)(T < cus ? T : cus);
     ts.xcd_split = (grid == cus && cus % 8 == 0 && T >= cus) ? 1 : 0;
     ts.per_xcd = grid / 8;

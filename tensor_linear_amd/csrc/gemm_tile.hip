@@ -553,19 +553,6 @@ void gemm_tile_kernel(GemmArgs g, TileSched ts, int vec_store, GemmExtra ex) {
 
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-int num_cus() {
-    static int n = 0;
-    if (n == 0) {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-            v > 0)
-            n = v;
-        else
-            n = 256;
-    }
-    return n;
-}
 
 // K per stage and number of stages (tuning parameters; 2 x 64 and 4 x 32 both
 // use 128 KB of LDS).
@@ -630,7 +617,7 @@ hipError_t launch_gemm_tile(const GemmArgs &g, int out_type, const GemmExtra *ex
     // +1.7-2.2% with 4; column products equal or better with 8).
     ts.group_m = out_type == OUT_BF16 ? 8 : 4;
     ts.T = (int)T;
-    const int cus = num_cus();
+    const int cus = device_cu_count();
     int grid = (int)(T < cus ? T : cus);
     ts.xcd_split = (grid == cus && cus % 8 == 0 && T >= cus) ? 1 : 0;
     ts.per_xcd = grid / 8;

@@ -115,4 +115,8 @@ hipError_t launch_embedding(const EmbedArgs &e, int elem_bytes, hipStream_t s);
 
 hipError_t launch_fill_zero(void *ptr, size_t words, hipStream_t s);
 
+// Compute units of the current device (cached per device; 256 if the query
+// fails).  Sizes the persistent grids of the tile kernels.
+int device_cu_count();
+
 }  // namespace tpl

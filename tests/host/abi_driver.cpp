@@ -23,6 +23,7 @@ hipError_t launch_gemm_rowfold(const GemmArgs &, const ReduceArgs &, hipStream_t
 bool gemm_rowfold_supported(const GemmArgs &, const ReduceArgs &) { std::abort(); }
 hipError_t launch_embedding(const EmbedArgs &, int, hipStream_t) { std::abort(); }
 hipError_t launch_fill_zero(void *, size_t, hipStream_t) { std::abort(); }
+int device_cu_count() { std::abort(); }
 }  // namespace tpl
 
 static int failures = 0;
