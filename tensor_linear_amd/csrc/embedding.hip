@@ -12,11 +12,13 @@
 // One wavefront per (token, shard) piece, consecutive wavefronts taking the
 // shards of one token in order, so the pieces of an output row are written
 // by neighbouring wavefronts.  Each lane moves 16 bytes per pass (one 1 KB
-// run per wavefront instruction).  Many small wavefronts keep the most reads
-// in flight: for 4096 tokens x 8 shards of 1 KB this takes 11.3 us per launch
-// (5.9 TB/s), against 19.5 us with eight pieces per wavefront (all eight
-// loads issued before the stores) and 15.3 us with non-temporal loads.  An id
-// outside [0, V) gives a zero piece and sets the caller's flag.
+// run per wavefront instruction); loads and stores are non-temporal, since
+// every byte is touched once.  For 4096 tokens x 8 shards of 1 KB at random
+// rows of 128 MB tables this takes ~15 us per launch (4.4 TB/s), the rate of
+// random 1 KB reads from HBM: two, four or eight pieces per wavefront (all
+// loads before the stores) ran 16.2, 20.3 and 47.4 us, 64- or 1024-thread
+// workgroups the same as 256.  An id outside [0, V) gives a zero piece and
+// sets the caller's flag.
 #include "kernels.h"
 
 #include <type_traits>
@@ -46,7 +48,7 @@ void embedding_vec(EmbedArgs e, int es) {
     }
     const char *src = (const char *)e.e_shard[i] + id * e.lde * es;
     for (int64_t o = (int64_t)lane * 16; o < bytes; o += 1024) {
-        const u32x4 v = *(const u32x4 *)(src + o);
+        const u32x4 v = __builtin_nontemporal_load((const u32x4 *)(src + o));
         __builtin_nontemporal_store(v, (u32x4 *)(y + o));
     }
 }
