@@ -195,32 +195,40 @@ class Workload:
         self.single = self._single_shard_ops(P, torch, tl)
 
     def _single_shard_ops(self, P, torch, tl):
-        """Shard 0 of each GEMM alone, at its real shape (one GPU's share of
-        the layer): (name, flop, bytes, fn).  Timed outside the step."""
+        """Each GEMM's shards launched alone, one at a time, at their real
+        shape (one GPU's share of the layer): (name, flop, bytes, fns) with
+        one launch function per shard.  The timer takes the shards in turn,
+        so a shard's operands (58.7 MB for a decode shard) are not still in
+        the 256 MB last-level cache from the launch before.  Timed outside
+        the step."""
         dev, bf = "cuda:0", torch.bfloat16
         ops = []
         def col(name, X, W):
             Ns = W.shape[0] // P
             Y = torch.empty((X.shape[0], Ns), dtype=bf, device=dev)
-            Wi = W[:Ns]
             fl = 2.0 * X.shape[0] * Ns * X.shape[1]
-            nb = (Wi.numel() + X.numel() + Y.numel()) * 2
-            ops.append((name, fl, nb, lambda: tl.tp_linear_column(X, Wi, Y, 1)))
+            nb = (Ns * X.shape[1] + X.numel() + Y.numel()) * 2
+            fns = [lambda Wi=W[i * Ns:(i + 1) * Ns]: tl.tp_linear_column(X, Wi, Y, 1)
+                   for i in range(P)]
+            ops.append((name, fl, nb, fns))
         def row(name, X, W, fused):
             Ks = X.shape[1] // P
-            Xi, Wi = X[:, :Ks], W[:, :Ks]
             M, N = X.shape[0], W.shape[0]
+            sl = [(X[:, i * Ks:(i + 1) * Ks], W[:, i * Ks:(i + 1) * Ks]) for i in range(P)]
             fl = 2.0 * M * N * Ks
             if fused:
                 Y = torch.empty((M, N), dtype=bf, device=dev)
                 ws = torch.empty(tl.tp_row_workspace_bytes(tl.TP_ROW_FUSED, M, N, 1),
                                  dtype=torch.uint8, device=dev)
-                nb = (Wi.numel() + Xi.numel() + Y.numel()) * 2
-                ops.append((name, fl, nb, lambda: tl.tp_linear_row(Xi, Wi, Y, 1, tl.TP_ROW_FUSED, ws)))
+                nb = (N * Ks + M * Ks + Y.numel()) * 2
+                fns = [lambda a=a, b=b: tl.tp_linear_row(a, b, Y, 1, tl.TP_ROW_FUSED, ws)
+                       for a, b in sl]
             else:
                 part = torch.empty((1, M, N), dtype=torch.float32, device=dev)
-                nb = (Wi.numel() + Xi.numel()) * 2 + part.numel() * 4
-                ops.append((name, fl, nb, lambda: tl.tp_linear_row(Xi, Wi, part, 1, tl.TP_ROW_PARTIAL)))
+                nb = (N * Ks + M * Ks) * 2 + part.numel() * 4
+                fns = [lambda a=a, b=b: tl.tp_linear_row(a, b, part, 1, tl.TP_ROW_PARTIAL)
+                       for a, b in sl]
+            ops.append((name, fl, nb, fns))
         if self.wid in (2, 3):
             col("column_gemm_one_shard", self.X1, self.W1)
             row("row_gemm_one_shard", self.X2, self.W2, False)
@@ -231,7 +239,7 @@ class Workload:
             wsf = torch.empty(tl.tp_row_workspace_bytes(tl.TP_ROW_FUSED, M, N, P),
                               dtype=torch.uint8, device=dev)
             ops.append(("row_layer_fused_fold_all_shards", 2.0 * M * N * self.X2.shape[1], None,
-                        lambda: tl.tp_linear_row(self.X2, self.W2, Yf, P, tl.TP_ROW_FUSED, wsf)))
+                        [lambda: tl.tp_linear_row(self.X2, self.W2, Yf, P, tl.TP_ROW_FUSED, wsf)]))
         elif self.wid == 4:
             col("column_gemm_decode_one_shard", self.X1, self.W1)
             row("row_gemm_decode_one_shard", self.X2, self.W2, True)
@@ -239,12 +247,12 @@ class Workload:
             X, W, b = self.X1, self.W1, self.b1
             Ns = W.shape[0] // P
             Hs = torch.empty((X.shape[0], Ns // 2), dtype=bf, device=dev)
-            Wi, bi = W[:Ns], b[:Ns]
             fl = 2.0 * X.shape[0] * Ns * X.shape[1]
-            nb = (Wi.numel() + X.numel() + Hs.numel()) * 2
-            ops.append(("column_gemm_swiglu_bias_one_shard", fl, nb,
-                        lambda: tl.tp_linear_column_ex(X, Wi, Hs, 1, bias=bi,
-                                                       act=tl.TP_ACT_SWIGLU)))
+            nb = (Ns * X.shape[1] + X.numel() + Hs.numel()) * 2
+            fns = [lambda Wi=W[i * Ns:(i + 1) * Ns], bi=b[i * Ns:(i + 1) * Ns]:
+                   tl.tp_linear_column_ex(X, Wi, Hs, 1, bias=bi, act=tl.TP_ACT_SWIGLU)
+                   for i in range(P)]
+            ops.append(("column_gemm_swiglu_bias_one_shard", fl, nb, fns))
             row("row_gemm_one_shard", self.H, self.W2, False)
         elif self.wid in (5, 7):
             row("row_gemm_one_shard", self.X1, self.W1, False)
@@ -498,17 +506,18 @@ def main():
     # Context, outside the timed step: each GEMM's shard 0 alone at its real
     # shape, and a plain device copy of 1 GiB.
     single = {}
-    for name, fl, nb, fn in wl.single:
-        for _ in range(3):
-            fn()
+    for name, fl, nb, fns in wl.single:
+        for r in range(3):
+            fns[r % len(fns)]()
         torch.cuda.synchronize()
+        reps = max(10, len(fns))
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        for _ in range(10):
-            fn()
+        for r in range(reps):
+            fns[r % len(fns)]()
         e1.record()
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) / 10 * 1e3
+        us = e0.elapsed_time(e1) / reps * 1e3
         single[name] = dict(avg_us=us, tflops=fl / us / 1e6,
                             frac_bf16_peak=fl / us / 1e6 / PEAK_BF16_TFLOPS)
         if nb:
@@ -566,8 +575,9 @@ def main():
         "context": {"one_shard": single,
                     "device_copy_gbps": copy_gbps,
                     "shader_clock_ghz": clocks,
-                    "note": "one_shard: shard 0 of each GEMM launched alone at its real shape "
-                            "(one GPU's share), and for the prefill workloads the whole row layer "
+                    "note": "one_shard: each GEMM's shards launched alone at their real shape "
+                            "(one GPU's share), one after another (so a shard is not still "
+                            "cached from the launch before), and for the prefill workloads the whole row layer "
                             "with the fold inside the GEMM (TP_ROW_FUSED); device_copy_gbps: read+write bytes of a 1 GiB "
                             "device-to-device copy per second; shader_clock_ghz: the shader "
                             "clock idle, while each GEMM of the step runs back to back (2.5 ms "
