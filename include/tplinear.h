@@ -48,7 +48,8 @@ extern "C" {
 typedef enum {
     TP_OK = 0,
     TP_ERR_NULL = 1,         /* a required pointer is NULL                          */
-    TP_ERR_SHAPE = 2,        /* negative size, leading dim too small, P out of range */
+    TP_ERR_SHAPE = 2,        /* negative size, leading dim too small, P out of range,
+                                a buffer of more than 2^60 elements (or workspace bytes) */
     TP_ERR_INDIVISIBLE = 3,  /* the split dim is not a multiple of P                 */
     TP_ERR_PLACEMENT = 4,    /* unknown placement kind, or dim out of range          */
     TP_ERR_DTYPE = 5,        /* unknown dtype                                        */
@@ -319,7 +320,8 @@ tp_status tp_embedding(const int64_t *ids, int64_t T, const void *E,
                        int32_t *bad_flag, void *stream);
 
 /* Bytes of workspace tp_linear_row needs for (mode, M, N, P); 0 for
- * TP_ROW_PARTIAL, and for invalid arguments. */
+ * TP_ROW_PARTIAL, and for invalid arguments (including P*M*N*4 > 2^60,
+ * which tp_linear_row rejects with TP_ERR_SHAPE). */
 size_t tp_row_workspace_bytes(int32_t mode, int64_t M, int64_t N, int32_t P);
 
 /* Queue a fill of `bytes` bytes (a multiple of 4) at `ptr` with zero, with a

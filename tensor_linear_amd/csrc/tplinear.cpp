@@ -19,12 +19,24 @@ inline bool valid_dtype(int32_t d) { return d == TP_F32 || d == TP_BF16; }
 
 inline tp_status hip_status(hipError_t e) { return e == hipSuccess ? TP_OK : TP_ERR_HIP; }
 
+// Largest element (or byte) count the library accepts for one buffer: every
+// offset and size it derives then fits in int64 / size_t without wrapping.
+constexpr int64_t MAX_EXTENT = (int64_t)1 << 60;
+
+// a * b * c <= MAX_EXTENT for non-negative a, b, c, without overflow.
+inline bool extent_ok(int64_t a, int64_t b, int64_t c = 1) {
+    int64_t ab, abc;
+    return !__builtin_mul_overflow(a, b, &ab) && !__builtin_mul_overflow(ab, c, &abc) &&
+           abc <= MAX_EXTENT;
+}
+
 // Common size checks of the two Linear entry points.
 tp_status check_gemm_shape(int64_t M, int64_t N, int64_t K, int32_t P, int64_t ldx,
                            int64_t ldw) {
     if (M < 0 || N < 0 || K < 0) return TP_ERR_SHAPE;
     if (P < 1 || P > TP_MAX_SHARDS) return TP_ERR_SHAPE;
     if (ldx < K || ldw < K || ldx < 1 || ldw < 1) return TP_ERR_SHAPE;
+    if (!extent_ok(M, ldx) || !extent_ok(N, ldw)) return TP_ERR_SHAPE;
     return TP_OK;
 }
 
@@ -50,7 +62,10 @@ void set_out_slices(ReduceArgs &r, void *const *y_slices, int32_t P) {
     for (int j = 0; j < MAX_SLICES; ++j) r.y_slice[j] = (y_slices && j < P) ? y_slices[j] : nullptr;
 }
 
+// Bytes of P fp32 [M, N] partials, rounded up; 0 when the count would pass
+// MAX_EXTENT (the callers reject those sizes).
 size_t partials_bytes(int64_t M, int64_t N, int32_t P) {
+    if (!extent_ok(M, N, (int64_t)P * (int64_t)sizeof(float))) return 0;
     return round_up((size_t)P * (size_t)M * (size_t)N * sizeof(float), WS_ALIGN);
 }
 
@@ -79,6 +94,7 @@ tp_status tp_shard_layout(int64_t rows, int64_t cols, int64_t ld, tp_placement p
                           tp_view *views) {
     if (!views) return TP_ERR_NULL;
     if (rows < 0 || cols < 0 || ld < cols || P < 1 || P > TP_MAX_SHARDS) return TP_ERR_SHAPE;
+    if (!extent_ok(rows, ld, pl.kind == TP_PARTIAL ? P : 1)) return TP_ERR_SHAPE;
     if (pl.kind == TP_SHARD) {
         int d = pl.dim;
         if (d < 0) d += 2;
@@ -128,6 +144,7 @@ tp_status tp_linear_column_ex(const void *X, const void *const *x_slices, int64_
     if (x_slices && M % P != 0) return TP_ERR_INDIVISIBLE;
     if (y_mode == TP_Y_CONCAT ? ldy < On * P : ldy < On) return TP_ERR_SHAPE;
     if (ldy < 1) return TP_ERR_SHAPE;
+    if (!extent_ok(M, ldy, y_mode == TP_Y_SHARDS ? P : 1)) return TP_ERR_SHAPE;
     if (M == 0 || N == 0) return TP_OK;
     if (!Y) return TP_ERR_NULL;
     if (K > 0) {
@@ -188,6 +205,9 @@ tp_status tp_linear_row_ex(const void *X, int64_t ldx, const void *W, int64_t ld
     if (mode == TP_ROW_SCATTER && M % P != 0) return TP_ERR_INDIVISIBLE;
     if (ldy < N || ldy < 1) return TP_ERR_SHAPE;
     if (y_slice_stride < 0) return TP_ERR_SHAPE;
+    if (!extent_ok(M, ldy, mode == TP_ROW_PARTIAL ? P : 1) ||
+        !extent_ok(M, N, (int64_t)P * (int64_t)sizeof(float)) || !extent_ok(P, y_slice_stride))
+        return TP_ERR_SHAPE;
     if (M == 0 || N == 0) return TP_OK;
     if (y_slices) {
         for (int32_t j = 0; j < P; ++j)
@@ -267,6 +287,9 @@ tp_status tp_shard_reduce_ex(const float *partials, int64_t shard_stride, int64_
     if (M < 0 || N < 0 || P < 1 || P > TP_MAX_SHARDS) return TP_ERR_SHAPE;
     if (ldp < N || ldy < N || ldp < 1 || ldy < 1 || shard_stride < 0 || y_slice_stride < 0)
         return TP_ERR_SHAPE;
+    if (!extent_ok(M, ldp) || !extent_ok(M, ldy) || !extent_ok(P, shard_stride) ||
+        !extent_ok(P, y_slice_stride))
+        return TP_ERR_SHAPE;
     if (!valid_dtype(out_dtype)) return TP_ERR_DTYPE;
     if (scatter != 0 && scatter != 1) return TP_ERR_MODE;
     if (y_slices && !scatter) return TP_ERR_MODE;
@@ -314,6 +337,8 @@ tp_status tp_embedding(const int64_t *ids, int64_t T, const void *E, const void 
     if (lde < 1) return TP_ERR_SHAPE;
     if (y_mode == TP_Y_CONCAT ? ldy < D : ldy < Ds) return TP_ERR_SHAPE;
     if (ldy < 1) return TP_ERR_SHAPE;
+    if (!extent_ok(V, lde) || !extent_ok(T, ldy, y_mode == TP_Y_SHARDS ? P : 1))
+        return TP_ERR_SHAPE;
     if (T == 0 || D == 0) return TP_OK;
     if (!ids || !Y || (E != nullptr) == (e_shards != nullptr)) return TP_ERR_NULL;
     EmbedArgs e;

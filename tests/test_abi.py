@@ -191,6 +191,30 @@ def test_reduce_errors():
     assert red(M=0) == tl.TP_OK
 
 
+def test_oversized_extents_rejected():
+    # Sizes whose element counts pass 2^60 are rejected before any size
+    # arithmetic can wrap: in particular a wrapped workspace size must never
+    # let a too-small workspace through.
+    big = 1 << 31
+    assert tl.tp_row_workspace_bytes(tl.TP_ROW_SUM, big, big, 8) == 0
+    assert tl.tp_row_workspace_bytes(tl.TP_ROW_SUM, 1 << 62, 1 << 62, 8) == 0
+    assert row(M=big, N=big, ldy=big) == tl.TP_ERR_SHAPE
+    assert row(M=1 << 62, N=1 << 62, ldy=1 << 62) == tl.TP_ERR_SHAPE
+    assert row(M=4, N=12, ldy=12, ldx=1 << 62, ldw=8) == tl.TP_ERR_SHAPE
+    assert row(mode=tl.TP_ROW_SCATTER, ss=1 << 62) == tl.TP_ERR_SHAPE
+    assert col(M=1 << 40, ldx=1 << 40) == tl.TP_ERR_SHAPE
+    assert col(M=1 << 40, ldy=1 << 40) == tl.TP_ERR_SHAPE
+    assert red(ss=1 << 62) == tl.TP_ERR_SHAPE
+    assert red(M=1 << 40, ldp=1 << 40) == tl.TP_ERR_SHAPE
+    views = (tl.tp_view * 4)()
+    assert tl.lib.tp_shard_layout(1 << 40, 4, 1 << 40, tl.tp_placement(tl.TP_SHARD, 0), 2,
+                                  views) == tl.TP_ERR_SHAPE
+    assert tl.lib.tp_shard_layout(1 << 31, 4, 1 << 30, tl.tp_placement(tl.TP_PARTIAL, 0), 4,
+                                  views) == tl.TP_ERR_SHAPE
+    # the largest accepted sizes still pass the checks (empty N: nothing queued)
+    assert row(M=1 << 20, N=0, ldy=1) == tl.TP_OK
+
+
 def test_workspace_zero_errors():
     assert tl.lib.tp_workspace_zero(None, 16, None) == tl.TP_ERR_NULL
     assert tl.lib.tp_workspace_zero(FWS, 6, None) == tl.TP_ERR_SHAPE
