@@ -155,6 +155,24 @@ def _mat(t, name):
     return t.data_ptr(), t.shape[0], t.shape[1], max(ld, t.shape[1], 1)
 
 
+def _same_gpu(*items):
+    """Every tensor given (lists of tensors included, None skipped) must live
+    on one GPU: the kernels dereference the data pointers on that device, so
+    a host tensor or a second device is rejected here, before any launch."""
+    dev = None
+    for it in items:
+        for t in (it if isinstance(it, (list, tuple)) else (it,)):
+            if t is None:
+                continue
+            if not t.is_cuda:
+                raise ValueError("every tensor must be a GPU tensor (got one on "
+                                 f"{t.device})")
+            if dev is None:
+                dev = t.device
+            elif t.device != dev:
+                raise ValueError(f"tensors on {dev} and {t.device}: all must share one GPU")
+
+
 def _ptr_array(ts, name):
     """Host array of the data pointers of a list of tensors (or None)."""
     if ts is None:
@@ -195,6 +213,7 @@ def tp_shard_layout(rows: int, cols: int, ld: int, kind: int, dim: int, P: int) 
 def tp_linear_column(X, W, Y, P: int, y_mode: int = TP_Y_CONCAT, stream=None) -> None:
     """Column-parallel Linear.  X [M, K], W [N, K]; Y [M, N] for TP_Y_CONCAT
     or [P, M, N/P] (block stride M*ldy) for TP_Y_SHARDS."""
+    _same_gpu(X, W, Y)
     xp, M, K, ldx = _mat(X, "X")
     wp, N, Kw, ldw = _mat(W, "W")
     if Kw != K:
@@ -220,6 +239,7 @@ def tp_row_workspace_bytes(mode: int, M: int, N: int, P: int) -> int:
 
 
 def tp_workspace_zero(buf, stream=None) -> None:
+    _same_gpu(buf)
     check(_get_lib().tp_workspace_zero(buf.data_ptr(), buf.numel() * buf.element_size(),
                                 _stream(buf, stream)))
 
@@ -231,6 +251,7 @@ def tp_linear_row(X, W, Y, P: int, mode: int = TP_ROW_SUM, workspace=None,
     [M, N] whose row blocks are the slices (y_slice_stride = 0), or a buffer
     with slice j at element offset j*y_slice_stride and rows [:M/P] of its
     2-D view Y."""
+    _same_gpu(X, W, Y, workspace)
     xp, M, K, ldx = _mat(X, "X")
     wp, N, Kw, ldw = _mat(W, "W")
     if Kw != K:
@@ -262,6 +283,7 @@ def tp_shard_reduce(partials, Y, P: int, scatter: int = 0, y_slice_stride: int =
                     stream=None) -> None:
     """Fold float32 partials [P, M, N] (or any [P, M, ldp] view) into Y [M, N]
     (scatter=0) or into P token slices (scatter=1)."""
+    _same_gpu(partials, Y)
     import torch
     if partials.dtype != torch.float32 or partials.dim() != 3 or partials.shape[0] != P:
         raise ValueError("partials must be float32 [P, M, N]")
@@ -279,6 +301,7 @@ def tp_linear_column_ex(X, W, Y, P: int, y_mode: int = TP_Y_CONCAT, bias=None,
     one row stride) is given.  W [N, K]; bias [N] or None.  Output columns per
     shard On = N/P, or N/(2P) with TP_ACT_SWIGLU; Y [M, P*On] for TP_Y_CONCAT
     or [P, M, On] for TP_Y_SHARDS."""
+    _same_gpu(X, W, Y, bias, x_slices)
     if (X is None) == (x_slices is None):
         raise ValueError("give exactly one of X and x_slices")
     if X is not None:
@@ -322,6 +345,7 @@ def tp_linear_row_ex(X, W, Y, P: int, mode: int = TP_ROW_SUM, workspace=None, bi
     for TP_ROW_SCATTER, token slices in separate tensors (y_slices: P tensors
     [M/P, N] with one row stride; Y is then None).  Otherwise as
     tp_linear_row."""
+    _same_gpu(X, W, Y, workspace, bias, y_slices)
     xp, M, K, ldx = _mat(X, "X")
     wp, N, Kw, ldw = _mat(W, "W")
     if Kw != K:
@@ -366,6 +390,7 @@ def tp_shard_reduce_ex(partials, Y, P: int, scatter: int = 0, bias=None, y_slice
                        y_slice_stride: int = 0, stream=None) -> None:
     """tp_shard_reduce with the row bias and, for scatter=1, token slices in
     separate tensors (y_slices: P tensors [M/P, N], one row stride; Y None)."""
+    _same_gpu(partials, Y, bias, y_slices)
     import torch
     if partials.dtype != torch.float32 or partials.dim() != 3 or partials.shape[0] != P:
         raise ValueError("partials must be float32 [P, M, N]")
@@ -398,6 +423,7 @@ def tp_embedding(ids, Y, P: int, E=None, e_shards=None, y_mode: int = TP_Y_CONCA
     [V, D/P], one row stride).  Y: [T, D] (TP_Y_CONCAT) or [P, T, D/P]
     (TP_Y_SHARDS).  bad: None or an int32 tensor set to 1 when an id is
     outside [0, V) (its output row is zero)."""
+    _same_gpu(ids, Y, E, e_shards, bad)
     import torch
     if ids.dtype != torch.int64 or ids.dim() != 1 or (ids.numel() > 1 and ids.stride(0) != 1):
         raise ValueError("ids must be a contiguous int64 [T] tensor")

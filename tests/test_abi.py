@@ -232,3 +232,25 @@ def test_binding_leading_dims():
     assert tl._mat(torch.zeros(0, 5), "Y")[1:] == (0, 5, 5)
     with pytest.raises(ValueError):
         tl._mat(torch.zeros(4, 6).t(), "Y")
+
+
+def test_binding_rejects_host_tensors():
+    """The kernels dereference device pointers: host tensors are refused by
+    the binding before the library is called."""
+    import torch
+    bf = torch.bfloat16
+    X, W, Y = torch.zeros(4, 8, dtype=bf), torch.zeros(12, 8, dtype=bf), torch.zeros(4, 12, dtype=bf)
+    parts = torch.zeros(4, 4, 12)
+    calls = [
+        lambda: tl.tp_linear_column(X, W, Y, 4),
+        lambda: tl.tp_linear_column_ex(X, W, Y, 4),
+        lambda: tl.tp_linear_row(X, W, Y, 4, tl.TP_ROW_SUM, torch.zeros(1 << 12, dtype=torch.uint8)),
+        lambda: tl.tp_linear_row_ex(X, W, parts, 4, tl.TP_ROW_PARTIAL),
+        lambda: tl.tp_shard_reduce(parts, Y, 4),
+        lambda: tl.tp_shard_reduce_ex(parts, Y, 4),
+        lambda: tl.tp_embedding(torch.zeros(4, dtype=torch.int64), Y, 4, E=W),
+        lambda: tl.tp_workspace_zero(torch.zeros(16, dtype=torch.uint8)),
+    ]
+    for c in calls:
+        with pytest.raises(ValueError, match="GPU tensor"):
+            c()
