@@ -303,7 +303,10 @@ hipError_t launch_gemm_skinny(const GemmArgs &g, int out_type, const FoldArgs *f
     // M = 16, K = 8192, N = 28672 over 8 shards: column 82-83 us with 3 or 4
     // stages of 256 columns against 88-89 with 2; fused fold of 8 shards of
     // K = 3584, N = 8192: 82-83 us with 32 columns and 3-6 stages, 86-87 with
-    // 16 columns and two 512-column stages.  The gated unit streams 32 W rows
+    // 16 columns and two 512-column stages; a later same-box sweep gave 86.6
+    // us for this choice against 85.9 (32 columns, 3 stages), 89.6-90.8 (16
+    // columns: 3 or 4 stages of 256, 2 of 512), 97.6 (32 columns, 2 stages of
+    // 512) and 147.7 (64 columns: half the CUs idle).  The gated unit streams 32 W rows
     // (16 gate, 16 up) per workgroup with the column form's stages.
     if (ex.act == ACT_SWIGLU) {
         if (fold) return hipErrorInvalidValue;
