@@ -116,20 +116,23 @@ class Workload:
             self.W2, self.b2 = nb(1, 1, (H, I), sw), nb(1, 2, (H,), sw)
             self.H = torch.empty((M, I), dtype=bf, device=dev)
             self.Y2 = torch.empty((M, H), dtype=bf, device=dev)
-            self.ws = torch.empty(tl.tp_row_workspace_bytes(tl.TP_ROW_FUSED, M, H, P),
-                                  dtype=torch.uint8, device=dev)
+            self.parts = torch.empty((P, M, H), dtype=torch.float32, device=dev)
+            # The row layer as the library runs TP_ROW_FUSED at this shape
+            # (shard K 1792, 4096 x 4096 output): fp32 partials, then the fold
+            # with the bias -- here faster than the fold in registers.
             self.ops = [
                 ("column_gemm_swiglu_bias", 2.0 * M * 2 * I * H, None,
                  lambda: tl.tp_linear_column_ex(self.X1, self.W1, self.H, P, bias=self.b1,
                                                 act=tl.TP_ACT_SWIGLU)),
-                ("row_gemm_fused_fold_bias", 2.0 * M * H * I, None,
-                 lambda: tl.tp_linear_row_ex(self.H, self.W2, self.Y2, P, tl.TP_ROW_FUSED,
-                                             self.ws, bias=self.b2)),
+                ("row_gemm", 2.0 * M * H * I, None,
+                 lambda: tl.tp_linear_row(self.H, self.W2, self.parts, P, tl.TP_ROW_PARTIAL)),
+                ("shard_fold_bias", 0.0, P * M * H * 4 + M * H * 2,
+                 lambda: tl.tp_shard_reduce_ex(self.parts, self.Y2, P, bias=self.b2)),
             ]
             self.name = ("Llama-8B MLP TP layer: M=4096, hidden 4096, intermediate 14336, P=8; "
                          "fc1 gate+up column 4096->2x14336 with Shard(0) bias and silu(gate)*up "
-                         "fused, fc2 row 14336->4096 on the gated output with the shard fold "
-                         "and the Partial bias inside the GEMM")
+                         "fused, fc2 row 14336->4096 on the gated output: fp32 shard partials, "
+                         "then the shard fold with the Partial bias added once")
             self.shape = dict(M=M, hidden=H, intermediate=I, P=P)
         elif wid == 8:
             T, V, D = 4096, 128256, 4096
@@ -232,13 +235,14 @@ class Workload:
         if self.wid in (2, 3):
             col("column_gemm_one_shard", self.X1, self.W1)
             row("row_gemm_one_shard", self.X2, self.W2, False)
-            # the whole row layer (all P shards) with the fold inside the GEMM,
-            # the alternative to row_gemm + shard_fold of the step
+            # the whole row layer (all P shards) through TP_ROW_FUSED, launched
+            # back to back: the library folds inside the GEMM where that is
+            # faster (the Llama-70B O layer), else runs partials + fold
             M, N = self.X2.shape[0], self.W2.shape[0]
             Yf = torch.empty((M, N), dtype=bf, device=dev)
             wsf = torch.empty(tl.tp_row_workspace_bytes(tl.TP_ROW_FUSED, M, N, P),
                               dtype=torch.uint8, device=dev)
-            ops.append(("row_layer_fused_fold_all_shards", 2.0 * M * N * self.X2.shape[1], None,
+            ops.append(("row_layer_tp_row_fused_all_shards", 2.0 * M * N * self.X2.shape[1], None,
                         [lambda: tl.tp_linear_row(self.X2, self.W2, Yf, P, tl.TP_ROW_FUSED, wsf)]))
         elif self.wid == 4:
             col("column_gemm_decode_one_shard", self.X1, self.W1)
@@ -313,7 +317,7 @@ def cpu_baseline(wl, rows, np, oracle, torch):
                 h_oracle = oracle.widen_bf16(oracle.round_bf16(Y.astype(np.float32)))
             parity[name] = dict(rows=r, rel_l2=oracle.rel_l2(got, Y),
                                 max_abs=oracle.max_abs(got, Y))
-        elif name in ("row_gemm", "row_gemm_fused_fold", "row_gemm_fused_fold_bias"):
+        elif name in ("row_gemm", "row_gemm_fused_fold"):
             X, W = (wl.X1, wl.W1) if wl.wid in (5, 7) else (getattr(wl, "X2", None), wl.W2)
             Mrows = wl.shape["M"]
             r = min(rows, Mrows)
@@ -578,7 +582,8 @@ def main():
                     "note": "one_shard: each GEMM's shards launched alone at their real shape "
                             "(one GPU's share), one after another (so a shard is not still "
                             "cached from the launch before), and for the prefill workloads the whole row layer "
-                            "with the fold inside the GEMM (TP_ROW_FUSED); device_copy_gbps: read+write bytes of a 1 GiB "
+                            "through TP_ROW_FUSED back to back (the fold inside the GEMM for the "
+                            "Llama-70B O layer, partials + fold for fc2); device_copy_gbps: read+write bytes of a 1 GiB "
                             "device-to-device copy per second; shader_clock_ghz: the shader "
                             "clock idle, while each GEMM of the step runs back to back (2.5 ms "
                             "window) and over a replay of the timed steps, from a probe kernel "

@@ -167,15 +167,17 @@ tp_status tp_linear_column(const void *X, int64_t ldx, const void *W, int64_t ld
  *   a running fp32 sum, so no partial reaches memory and the workspace is
  *   not touched.  That holds for bf16 operands (16-byte aligned, leading
  *   dims and shard offsets multiples of 8) with 1 <= M <= 64, or with K/P a
- *   multiple of 64 and at most 2048.  Other shapes run the TP_ROW_SUM
- *   sequence in the workspace, which is therefore always required.
+ *   multiple of 64 and at most 1280 (at most 1792 when M*N >= 8192*8192),
+ *   where the in-register fold measured faster.  Other shapes run the
+ *   TP_ROW_SUM sequence in the workspace, which is therefore always
+ *   required.
  * mode TP_ROW_SCATTER: requires M % P == 0.  Token slice j = rows
  *   [j*M/P, (j+1)*M/P) of the fold is written to Y + j*y_slice_stride with
  *   row stride ldy (y_slice_stride = 0 means (M/P)*ldy, the contiguous layout
  *   whose Shard(0) views are the slices).  The reduce-scatter over tokens.
- *   Bit for bit the rows of TP_ROW_SUM; for bf16 with K/P a multiple of 64,
- *   at most 2048, and M/P a multiple of 256 the fold runs inside the GEMM as
- *   for TP_ROW_FUSED and the workspace is not touched.
+ *   Bit for bit the rows of TP_ROW_SUM; for bf16 with K/P as for
+ *   TP_ROW_FUSED and M/P a multiple of 256 the fold runs inside the GEMM and
+ *   the workspace is not touched.
  * y_slice_stride is ignored by the other modes.
  * workspace: device memory of ws_bytes >= tp_row_workspace_bytes(mode, M, N, P),
  *   256-byte aligned.  May be NULL when that size is 0.  Calls that share a

@@ -257,14 +257,16 @@ tp_status tp_linear_row_ex(const void *X, int64_t ldx, const void *W, int64_t ld
         r.slice_stride = 0;
     }
     // Prefill shapes: the fold in registers (256x128 tiles walking the P
-    // shards) saves writing and re-reading the P fp32 partials; its narrower
-    // tile moves 1.5x the operand bytes per flop, which wins while the
-    // shard's K is short.  Measured on one box: fc2 K/P = 1792 460 vs 519 us,
-    // O K/P = 1024 955 vs 1404 us, sequence-parallel K/P = 3584 8431 vs
-    // 7347 us.
-    constexpr int64_t ROWFOLD_MAX_KS = 2048;
-    if ((mode == TP_ROW_FUSED || mode == TP_ROW_SCATTER) && dtype == TP_BF16 &&
-        Ks <= ROWFOLD_MAX_KS && gemm_rowfold_supported(g, r))
+    // shards) saves writing and re-reading the P fp32 partials, but its
+    // narrower tile moves 1.5x the operand bytes per flop, so it wins only
+    // while the shard's K is short -- the shorter, the smaller the output.
+    // Fused / unfused time measured on one box with cold caches (a 1 GiB
+    // write before each call), P = 8: M = N = 4096: K/P = 1024 0.88, 1280
+    // 0.95, 1536 1.03, 1792 1.08, 2048 1.08; M = N = 8192: 1024 0.77, 1280
+    // 0.87, 1536 0.94, 1792 0.95, 2048 1.03.
+    const bool fold_in_gemm = Ks <= 1280 || (Ks <= 1792 && M * N >= (int64_t)8192 * 8192);
+    if ((mode == TP_ROW_FUSED || mode == TP_ROW_SCATTER) && dtype == TP_BF16 && fold_in_gemm &&
+        gemm_rowfold_supported(g, r))
         return hip_status(launch_gemm_rowfold(g, r, s));
 
     hipError_t e = run_gemm(g, dtype, OUT_F32, nullptr, s);
