@@ -13,7 +13,7 @@ Prints ONE JSON line.  `value` is the step's GEMM TFLOP/s; `roofline` is for
 the dominant kernel (the fc1 column GEMM, MFMA-bound), its time measured with
 HIP events on the stream it runs on; `cpu_baseline` times the CPU oracle on a
 bounded sample of the same workload; `context` holds figures taken outside the
-timed step (each GEMM's shard 0 alone at its real shape, a plain device copy,
+timed step (each GEMM's shards launched alone, in turn, at their real shape, a plain device copy,
 the shader clock while each GEMM runs and the roofline fraction at that clock:
 the chip lowers its clock under sustained matrix-core load).
 
@@ -23,7 +23,9 @@ biases and the gated unit fused into the gate+up column GEMM (the row GEMM
 reads the gated output), 7 the sequence-parallel round trip with the token
 slices in P separate allocations (reduce-scatter writes them, the next column
 GEMM reads them in place), 8 the Llama-8B token embedding sharded on its
-feature dim (P shard tables in separate allocations, all-gathered output).
+feature dim (P shard tables in separate allocations, all-gathered output, a new
+batch of token ids every step; its one-kernel steps are timed as a replay of
+them captured in a HIP graph).
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload 2..8]
 """
