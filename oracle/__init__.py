@@ -371,12 +371,23 @@ def expected_views(rows: int, cols: int, ld: int, kind: int, dim: int, P: int) -
 
 
 # ---------------------------------------------------------------------------
-# O10: comparison metrics.
+# O10: comparison metrics behind every tolerance bar (the page "模型并行",
+# section "Tensor-parallel 线性层", compares the sharded result with the dense
+# product element by element).
 # ---------------------------------------------------------------------------
 
-def rel_l2(got: np.ndarray, ref: np.ndarray) -> float:
+def _pair(got, ref):
     g = np.asarray(got, dtype=np.float64)
     r = np.asarray(ref, dtype=np.float64)
+    if g.shape != r.shape:
+        raise ValueError(f"shape mismatch: got {g.shape}, ref {r.shape}")
+    return g, r
+
+
+def rel_l2(got: np.ndarray, ref: np.ndarray) -> float:
+    """||got - ref||_2 / ||ref||_2 in fp64 over all elements.  A zero ref
+    gives 0 when got equals it and +inf otherwise.  Shapes must match."""
+    g, r = _pair(got, ref)
     den = float(np.sqrt(np.sum(r * r)))
     num = float(np.sqrt(np.sum((g - r) ** 2)))
     if den == 0.0:
@@ -385,8 +396,8 @@ def rel_l2(got: np.ndarray, ref: np.ndarray) -> float:
 
 
 def max_abs(got: np.ndarray, ref: np.ndarray) -> float:
-    g = np.asarray(got, dtype=np.float64)
-    r = np.asarray(ref, dtype=np.float64)
+    """max |got - ref| in fp64 (0 for empty arrays).  Shapes must match."""
+    g, r = _pair(got, ref)
     if g.size == 0:
         return 0.0
     return float(np.max(np.abs(g - r)))

@@ -8,6 +8,9 @@ A plausible slip in the oracle fails at least one test here:
   * a wrong split offset or chunk size           -> index-map tests, identity W
   * a wrong fold order or extra rounding         -> the fold golden cases
   * a wrong rounding rule                        -> the bf16 golden cases
+  * a slip in the comparison metrics (a dropped square root, the norm of
+    the result instead of the reference's, a signed maximum, swapped
+    arguments, silent broadcasting)              -> the metric closed forms
 """
 import json
 import os
@@ -310,3 +313,50 @@ def test_index_sets_cover_exactly_once(R, C):
     for kind in (oracle.REPLICATE, oracle.PARTIAL):
         sets = oracle.shard_index_sets(R, C, kind, 0, 3)
         assert all(len(s) == R * C for s in sets)
+
+
+# ---------------------------------------------------------------------------
+# O10 metrics.  Every tolerance verdict goes through rel_l2 and max_abs, so
+# they are pinned to values worked out by hand from their definitions:
+# rel_l2 = ||got - ref||_2 / ||ref||_2, max_abs = max |got - ref|.
+# ---------------------------------------------------------------------------
+
+def test_rel_l2_closed_forms():
+    # one element off by d: |d| / ||ref||; ref (3, 4) has norm 5 exactly.
+    assert oracle.rel_l2([3.0, 6.0], [3.0, 4.0]) == 0.4        # ||got||: 2/sqrt(45)
+    assert oracle.rel_l2([3.0, 2.0], [3.0, 4.0]) == 0.4
+    # no square roots: 0.16 would be (d / ||ref||)^2
+    assert oracle.rel_l2([1.0, 2.0], [1.0, 1.0]) == pytest.approx(1 / np.sqrt(2), rel=1e-15)
+    # argument order matters: the reference's norm is the denominator
+    assert oracle.rel_l2([2.0], [1.0]) == 1.0
+    assert oracle.rel_l2([1.0], [2.0]) == 0.5
+    # a uniform relative error eps on every element gives exactly |eps|
+    ref = np.random.default_rng(7).standard_normal((17, 33))
+    for eps in (0.5, -0.25, 2.0 ** -10):
+        assert oracle.rel_l2(ref * (1 + eps), ref) == pytest.approx(abs(eps), rel=1e-12)
+    # zero reference: 0 when equal, infinite otherwise
+    assert oracle.rel_l2([0.0, 0.0], [0.0, 0.0]) == 0.0
+    assert oracle.rel_l2([3.0, 4.0], [0.0, 0.0]) == float("inf")
+    # all elements count, in any layout (2-D here)
+    assert oracle.rel_l2([[0.0, 3.0], [4.0, 5.0]], [[0.0, 3.0], [4.0, 0.0]]) == 1.0
+
+
+def test_max_abs_closed_forms():
+    assert oracle.max_abs([-5.0], [0.0]) == 5.0
+    assert oracle.max_abs([0.0], [-5.0]) == 5.0
+    # the largest magnitude, not the largest signed difference (that is 2)
+    assert oracle.max_abs([0.0, -3.0, 2.0], [0.0, 0.0, 0.0]) == 3.0
+    assert oracle.max_abs([[1.5, 1.0], [1.0, -7.0]], [[1.0, 1.0], [1.0, 1.0]]) == 8.0
+    assert oracle.max_abs(np.zeros((0, 4)), np.zeros((0, 4))) == 0.0
+
+
+def test_metrics_reject_shape_mismatch():
+    # got - ref must not broadcast: a (N,) result against a (rows, N)
+    # reference is a harness mistake, not a comparison.
+    for f in (oracle.rel_l2, oracle.max_abs):
+        with pytest.raises(ValueError):
+            f(np.zeros(4), np.zeros((3, 4)))
+        with pytest.raises(ValueError):
+            f(np.zeros((4, 1)), np.zeros((4, 4)))
+        with pytest.raises(ValueError):
+            f(np.zeros((2, 3)), np.zeros((3, 2)))
