@@ -174,7 +174,9 @@ tp_status tp_linear_column(const void *X, int64_t ldx, const void *W, int64_t ld
  * mode TP_ROW_SCATTER: requires M % P == 0.  Token slice j = rows
  *   [j*M/P, (j+1)*M/P) of the fold is written to Y + j*y_slice_stride with
  *   row stride ldy (y_slice_stride = 0 means (M/P)*ldy, the contiguous layout
- *   whose Shard(0) views are the slices).  The reduce-scatter over tokens.
+ *   whose Shard(0) views are the slices; a nonzero stride must be at least
+ *   (M/P - 1)*ldy + N, so that slices do not overlap, else TP_ERR_SHAPE).
+ *   The reduce-scatter over tokens.
  *   Bit for bit the rows of TP_ROW_SUM; for bf16 with K/P as for
  *   TP_ROW_FUSED and M/P a multiple of 256 the fold runs inside the GEMM and
  *   the workspace is not touched.
@@ -203,7 +205,8 @@ tp_status tp_linear_row(const void *X, int64_t ldx, const void *W, int64_t ldw,
  * scatter = 0: Y [M, N] of out_dtype, row stride ldy >= N.
  * scatter = 1: requires M % P == 0; slice j (rows [j*M/P, (j+1)*M/P)) at
  *   Y + j*y_slice_stride, row stride ldy (y_slice_stride = 0 means
- *   (M/P)*ldy).
+ *   (M/P)*ldy; a nonzero stride below (M/P - 1)*ldy + N, which would make
+ *   slices overlap, is TP_ERR_SHAPE).
  * Y = ((p_0 + p_1) + p_2) + ... + p_{P-1}, fp32 adds, then one rounding to
  *   bf16 (round to nearest even) for out_dtype TP_BF16.
  * Errors: TP_ERR_NULL, TP_ERR_SHAPE, TP_ERR_INDIVISIBLE, TP_ERR_DTYPE,

@@ -180,6 +180,53 @@ def _ptr_array(ts, name):
     return (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
 
 
+def _check_p(P):
+    if not 1 <= P <= TP_MAX_SHARDS:
+        check(TP_ERR_SHAPE)
+
+
+def _expect_shape(t, shape, name):
+    """The library writes exactly `shape`; a smaller or differently shaped
+    output would be written out of bounds, so it is refused here."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _expect_room(t, elems, name):
+    """t's storage must hold `elems` elements from t's first element."""
+    have = t.untyped_storage().nbytes() // t.element_size() - t.storage_offset()
+    if elems > have:
+        raise ValueError(f"{name}: the output needs {elems} elements from its first one, "
+                         f"its storage holds {have}")
+
+
+def _scatter_out(Y, M, N, P, scatter, y_slice_stride, name="Y"):
+    """Row stride of a fold / reduce-scatter output Y: [M, N], or for a
+    reduce-scatter with a nonzero slice stride the [M/P, N] view of slice 0
+    inside a buffer that holds all P slices."""
+    if scatter and M % P:
+        check(TP_ERR_INDIVISIBLE)
+    yp, _, _, ldy = _mat(Y, name)
+    if scatter and y_slice_stride:
+        s = M // P
+        _expect_shape(Y, (s, N), name)
+        if s and N:
+            _expect_room(Y, (P - 1) * y_slice_stride + (s - 1) * ldy + N, name)
+    else:
+        _expect_shape(Y, (M, N), name)
+    return yp, ldy
+
+
+def _block_out(Y, P, rows, cols, name="Y"):
+    """Pointer and row stride of a [P, rows, cols] output whose blocks are
+    rows*ldy elements apart."""
+    _expect_shape(Y, (P, rows, cols), name)
+    _, _, _, ldy = _mat(Y[0], f"{name}[0]")
+    if P > 1 and Y.stride(0) != rows * ldy:
+        raise ValueError(f"{name} blocks must be rows*ldy elements apart")
+    return Y.data_ptr(), ldy
+
+
 def _bias_ptr(bias, dt):
     if bias is None:
         return None
@@ -213,7 +260,6 @@ def tp_shard_layout(rows: int, cols: int, ld: int, kind: int, dim: int, P: int) 
 def tp_linear_column(X, W, Y, P: int, y_mode: int = TP_Y_CONCAT, stream=None) -> None:
     """Column-parallel Linear.  X [M, K], W [N, K]; Y [M, N] for TP_Y_CONCAT
     or [P, M, N/P] (block stride M*ldy) for TP_Y_SHARDS."""
-    _same_gpu(X, W, Y)
     xp, M, K, ldx = _mat(X, "X")
     wp, N, Kw, ldw = _mat(W, "W")
     if Kw != K:
@@ -221,15 +267,15 @@ def tp_linear_column(X, W, Y, P: int, y_mode: int = TP_Y_CONCAT, stream=None) ->
     dt = _dtype_code(X)
     if _dtype_code(W) != dt or _dtype_code(Y) != dt:
         raise TypeError("X, W and Y must share one dtype")
+    _check_p(P)
+    if N % P:
+        check(TP_ERR_INDIVISIBLE)
     if y_mode == TP_Y_SHARDS:
-        if Y.dim() != 3 or Y.shape[0] != P or Y.shape[1] != M:
-            raise ValueError("Y must be [P, M, N/P] for TP_Y_SHARDS")
-        yp, _, _, ldy = _mat(Y[0], "Y[0]")
-        if P > 1 and Y.stride(0) != M * ldy:
-            raise ValueError("Y blocks must be M*ldy elements apart")
-        yp = Y.data_ptr()
+        yp, ldy = _block_out(Y, P, M, N // P)
     else:
         yp, _, _, ldy = _mat(Y, "Y")
+        _expect_shape(Y, (M, N), "Y")
+    _same_gpu(X, W, Y)
     check(_get_lib().tp_linear_column(xp, ldx, wp, ldw, yp, ldy, y_mode, M, N, K, P, dt,
                                _stream(X, stream)))
 
@@ -251,7 +297,6 @@ def tp_linear_row(X, W, Y, P: int, mode: int = TP_ROW_SUM, workspace=None,
     [M, N] whose row blocks are the slices (y_slice_stride = 0), or a buffer
     with slice j at element offset j*y_slice_stride and rows [:M/P] of its
     2-D view Y."""
-    _same_gpu(X, W, Y, workspace)
     xp, M, K, ldx = _mat(X, "X")
     wp, N, Kw, ldw = _mat(W, "W")
     if Kw != K:
@@ -259,22 +304,21 @@ def tp_linear_row(X, W, Y, P: int, mode: int = TP_ROW_SUM, workspace=None,
     dt = _dtype_code(X)
     if _dtype_code(W) != dt:
         raise TypeError("X and W must share one dtype")
+    _check_p(P)
     if mode == TP_ROW_PARTIAL:
         import torch
-        if Y.dtype != torch.float32 or Y.dim() != 3 or Y.shape[0] != P:
+        if Y.dtype != torch.float32:
             raise ValueError("Y must be float32 [P, M, N] for TP_ROW_PARTIAL")
-        _, _, _, ldy = _mat(Y[0], "Y[0]")
-        if P > 1 and Y.stride(0) != M * ldy:
-            raise ValueError("Y parts must be M*ldy elements apart")
-        yp = Y.data_ptr()
+        yp, ldy = _block_out(Y, P, M, N)
     else:
         if _dtype_code(Y) != dt:
             raise TypeError("Y must have the dtype of X")
-        yp, _, _, ldy = _mat(Y, "Y")
+        yp, ldy = _scatter_out(Y, M, N, P, mode == TP_ROW_SCATTER, y_slice_stride)
     if workspace is not None:
         wsp, wsb = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     else:
         wsp, wsb = None, 0
+    _same_gpu(X, W, Y, workspace)
     check(_get_lib().tp_linear_row(xp, ldx, wp, ldw, yp, ldy, y_slice_stride, mode, wsp, wsb,
                             M, N, K, P, dt, _stream(X, stream)))
 
@@ -283,13 +327,14 @@ def tp_shard_reduce(partials, Y, P: int, scatter: int = 0, y_slice_stride: int =
                     stream=None) -> None:
     """Fold float32 partials [P, M, N] (or any [P, M, ldp] view) into Y [M, N]
     (scatter=0) or into P token slices (scatter=1)."""
-    _same_gpu(partials, Y)
     import torch
+    _check_p(P)
     if partials.dtype != torch.float32 or partials.dim() != 3 or partials.shape[0] != P:
         raise ValueError("partials must be float32 [P, M, N]")
     _, M, N, ldp = _mat(partials[0], "partials[0]")
     ss = partials.stride(0) if P > 1 else M * ldp
-    yp, _, _, ldy = _mat(Y, "Y")
+    yp, ldy = _scatter_out(Y, M, N, P, scatter, y_slice_stride)
+    _same_gpu(partials, Y)
     check(_get_lib().tp_shard_reduce(partials.data_ptr(), ss, ldp, yp, ldy, y_slice_stride, scatter,
                               M, N, P, _dtype_code(Y), _stream(partials, stream)))
 
@@ -301,7 +346,7 @@ def tp_linear_column_ex(X, W, Y, P: int, y_mode: int = TP_Y_CONCAT, bias=None,
     one row stride) is given.  W [N, K]; bias [N] or None.  Output columns per
     shard On = N/P, or N/(2P) with TP_ACT_SWIGLU; Y [M, P*On] for TP_Y_CONCAT
     or [P, M, On] for TP_Y_SHARDS."""
-    _same_gpu(X, W, Y, bias, x_slices)
+    _check_p(P)
     if (X is None) == (x_slices is None):
         raise ValueError("give exactly one of X and x_slices")
     if X is not None:
@@ -326,15 +371,17 @@ def tp_linear_column_ex(X, W, Y, P: int, y_mode: int = TP_Y_CONCAT, bias=None,
     dt = _dtype_code(ref)
     if _dtype_code(W) != dt or _dtype_code(Y) != dt:
         raise TypeError("X, W and Y must share one dtype")
+    if N % P or (act == TP_ACT_SWIGLU and (N // P) % 2):
+        check(TP_ERR_INDIVISIBLE)
+    On = N // P // 2 if act == TP_ACT_SWIGLU else N // P
+    if bias is not None:
+        _expect_shape(bias, (N,), "bias")
     if y_mode == TP_Y_SHARDS:
-        if Y.dim() != 3 or Y.shape[0] != P or Y.shape[1] != M:
-            raise ValueError("Y must be [P, M, On] for TP_Y_SHARDS")
-        yp, _, _, ldy = _mat(Y[0], "Y[0]")
-        if P > 1 and Y.stride(0) != M * ldy:
-            raise ValueError("Y blocks must be M*ldy elements apart")
-        yp = Y.data_ptr()
+        yp, ldy = _block_out(Y, P, M, On)
     else:
         yp, _, _, ldy = _mat(Y, "Y")
+        _expect_shape(Y, (M, P * On), "Y")
+    _same_gpu(X, W, Y, bias, x_slices)
     check(_get_lib().tp_linear_column_ex(xp, sl, ldx, wp, ldw, _bias_ptr(bias, dt), yp, ldy,
                                          y_mode, act, M, N, K, P, dt, _stream(ref, stream)))
 
@@ -345,7 +392,7 @@ def tp_linear_row_ex(X, W, Y, P: int, mode: int = TP_ROW_SUM, workspace=None, bi
     for TP_ROW_SCATTER, token slices in separate tensors (y_slices: P tensors
     [M/P, N] with one row stride; Y is then None).  Otherwise as
     tp_linear_row."""
-    _same_gpu(X, W, Y, workspace, bias, y_slices)
+    _check_p(P)
     xp, M, K, ldx = _mat(X, "X")
     wp, N, Kw, ldw = _mat(W, "W")
     if Kw != K:
@@ -353,12 +400,16 @@ def tp_linear_row_ex(X, W, Y, P: int, mode: int = TP_ROW_SUM, workspace=None, bi
     dt = _dtype_code(X)
     if _dtype_code(W) != dt:
         raise TypeError("X and W must share one dtype")
+    if bias is not None:
+        _expect_shape(bias, (N,), "bias")
     ys = None
     if y_slices is not None:
         if Y is not None:
             raise ValueError("give Y or y_slices, not both")
         if len(y_slices) != P:
             raise ValueError(f"y_slices must hold P={P} tensors")
+        if M % P:
+            check(TP_ERR_INDIVISIBLE)
         _, _, _, ldy = _mat(y_slices[0], "y_slices[0]")
         for j, t in enumerate(y_slices):
             _, mj, nj, lj = _mat(t, f"y_slices[{j}]")
@@ -367,20 +418,18 @@ def tp_linear_row_ex(X, W, Y, P: int, mode: int = TP_ROW_SUM, workspace=None, bi
         yp, ys = None, _ptr_array(y_slices, "y_slices")
     elif mode == TP_ROW_PARTIAL:
         import torch
-        if Y.dtype != torch.float32 or Y.dim() != 3 or Y.shape[0] != P:
+        if Y.dtype != torch.float32:
             raise ValueError("Y must be float32 [P, M, N] for TP_ROW_PARTIAL")
-        _, _, _, ldy = _mat(Y[0], "Y[0]")
-        if P > 1 and Y.stride(0) != M * ldy:
-            raise ValueError("Y parts must be M*ldy elements apart")
-        yp = Y.data_ptr()
+        yp, ldy = _block_out(Y, P, M, N)
     else:
         if _dtype_code(Y) != dt:
             raise TypeError("Y must have the dtype of X")
-        yp, _, _, ldy = _mat(Y, "Y")
+        yp, ldy = _scatter_out(Y, M, N, P, mode == TP_ROW_SCATTER, y_slice_stride)
     if workspace is not None:
         wsp, wsb = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     else:
         wsp, wsb = None, 0
+    _same_gpu(X, W, Y, workspace, bias, y_slices)
     check(_get_lib().tp_linear_row_ex(xp, ldx, wp, ldw, _bias_ptr(bias, dt), yp, ys, ldy,
                                       y_slice_stride, mode, wsp, wsb, M, N, K, P, dt,
                                       _stream(X, stream)))
@@ -390,17 +439,21 @@ def tp_shard_reduce_ex(partials, Y, P: int, scatter: int = 0, bias=None, y_slice
                        y_slice_stride: int = 0, stream=None) -> None:
     """tp_shard_reduce with the row bias and, for scatter=1, token slices in
     separate tensors (y_slices: P tensors [M/P, N], one row stride; Y None)."""
-    _same_gpu(partials, Y, bias, y_slices)
     import torch
+    _check_p(P)
     if partials.dtype != torch.float32 or partials.dim() != 3 or partials.shape[0] != P:
         raise ValueError("partials must be float32 [P, M, N]")
     _, M, N, ldp = _mat(partials[0], "partials[0]")
     ss = partials.stride(0) if P > 1 else M * ldp
+    if bias is not None:
+        _expect_shape(bias, (N,), "bias")
     if y_slices is not None:
         if Y is not None:
             raise ValueError("give Y or y_slices, not both")
         if len(y_slices) != P:
             raise ValueError(f"y_slices must hold P={P} tensors")
+        if M % P:
+            check(TP_ERR_INDIVISIBLE)
         _, _, _, ldy = _mat(y_slices[0], "y_slices[0]")
         odt = _dtype_code(y_slices[0])
         for j, t in enumerate(y_slices):
@@ -409,8 +462,9 @@ def tp_shard_reduce_ex(partials, Y, P: int, scatter: int = 0, bias=None, y_slice
                 raise ValueError("y_slices must be [M/P, N] of one dtype and row stride")
         yp, ys = None, _ptr_array(y_slices, "y_slices")
     else:
-        yp, _, _, ldy = _mat(Y, "Y")
+        yp, ldy = _scatter_out(Y, M, N, P, scatter, y_slice_stride)
         odt, ys = _dtype_code(Y), None
+    _same_gpu(partials, Y, bias, y_slices)
     check(_get_lib().tp_shard_reduce_ex(partials.data_ptr(), ss, ldp, _bias_ptr(bias, odt), yp,
                                         ys, ldy, y_slice_stride, scatter, M, N, P, odt,
                                         _stream(partials, stream)))
@@ -423,8 +477,8 @@ def tp_embedding(ids, Y, P: int, E=None, e_shards=None, y_mode: int = TP_Y_CONCA
     [V, D/P], one row stride).  Y: [T, D] (TP_Y_CONCAT) or [P, T, D/P]
     (TP_Y_SHARDS).  bad: None or an int32 tensor set to 1 when an id is
     outside [0, V) (its output row is zero)."""
-    _same_gpu(ids, Y, E, e_shards, bad)
     import torch
+    _check_p(P)
     if ids.dtype != torch.int64 or ids.dim() != 1 or (ids.numel() > 1 and ids.stride(0) != 1):
         raise ValueError("ids must be a contiguous int64 [T] tensor")
     T = ids.shape[0]
@@ -445,16 +499,15 @@ def tp_embedding(ids, Y, P: int, E=None, e_shards=None, y_mode: int = TP_Y_CONCA
         ep, D, es = None, Ds * P, _ptr_array(e_shards, "e_shards")
     if _dtype_code(Y) != dt:
         raise TypeError("Y must have the table's dtype")
+    if D % P:
+        check(TP_ERR_INDIVISIBLE)
     if y_mode == TP_Y_SHARDS:
-        if Y.dim() != 3 or Y.shape[0] != P or Y.shape[1] != T:
-            raise ValueError("Y must be [P, T, D/P] for TP_Y_SHARDS")
-        _, _, _, ldy = _mat(Y[0], "Y[0]")
-        if P > 1 and Y.stride(0) != T * ldy:
-            raise ValueError("Y blocks must be T*ldy elements apart")
-        yp = Y.data_ptr()
+        yp, ldy = _block_out(Y, P, T, D // P)
     else:
         yp, _, _, ldy = _mat(Y, "Y")
+        _expect_shape(Y, (T, D), "Y")
     if bad is not None and (bad.dtype != torch.int32 or bad.numel() < 1):
         raise ValueError("bad must be an int32 tensor")
+    _same_gpu(ids, Y, E, e_shards, bad)
     check(_get_lib().tp_embedding(ids.data_ptr(), T, ep, es, lde, V, D, yp, ldy, y_mode, P, dt,
                                   None if bad is None else bad.data_ptr(), _stream(ids, stream)))

@@ -360,7 +360,10 @@ hipError_t launch_gemm_rowfold(const GemmArgs &g, const ReduceArgs &ro, hipStrea
     ts.xcd_split = (grid == cus && cus % 8 == 0 && T >= cus) ? 1 : 0;
     ts.per_xcd = grid / 8;
     bool vec = ro.ldy % 8 == 0;
-    const bool scat = ro.slice_rows < g.M;
+    // Slice addressing whenever the output is split into slices or given as
+    // slice allocations (with one slice, P = 1, slice 0 is the whole output
+    // and ro.Y is not set).
+    const bool scat = ro.use_slices || ro.slice_rows < g.M;
     if (scat && ro.use_slices) {
         for (int64_t j = 0; j * ro.slice_rows < g.M; ++j) vec = vec && aligned16(ro.y_slice[j]);
     } else {

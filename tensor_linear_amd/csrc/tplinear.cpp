@@ -40,6 +40,30 @@ tp_status check_gemm_shape(int64_t M, int64_t N, int64_t K, int32_t P, int64_t l
     return TP_OK;
 }
 
+// A reduce-scatter's slice stride: 0 (the slices are the row blocks of Y)
+// or at least the extent of one slice, (rows - 1) * ldy + N elements, so that
+// no two slices share an element (shared elements would be written by two
+// workgroups in no fixed order).
+inline bool slice_stride_ok(int64_t stride, int64_t rows, int64_t N, int64_t ldy) {
+    if (stride == 0 || rows == 0 || N == 0) return true;
+    return stride >= (rows - 1) * ldy + N;
+}
+
+// Element distance between consecutive shard views of a placement over a
+// [rows, cols] tensor with row stride ld.  The launch path addresses shard i
+// at base + i * stride, so the stride is read off tp_shard_layout's own views
+// (and checked to be uniform): the views the kernels touch are exactly the
+// ones the layout entry point reports.  -1 if the layout rejects the shape.
+int64_t view_stride(int64_t rows, int64_t cols, int64_t ld, int32_t kind, int32_t dim,
+                    int32_t P) {
+    tp_view v[TP_MAX_SHARDS];
+    if (tp_shard_layout(rows, cols, ld, tp_placement{kind, dim}, P, v) != TP_OK) return -1;
+    const int64_t stride = P > 1 ? v[1].elem_offset - v[0].elem_offset : 0;
+    for (int32_t i = 0; i < P; ++i)
+        if (v[i].elem_offset != i * stride) return -1;
+    return stride;
+}
+
 // Run one grouped shard GEMM with the best kernel that takes it.
 // Decode-shaped bf16 problems (M <= 64) stream W with the skinny kernel;
 // large aligned bf16 problems use the 256x256 MFMA tile kernel; everything
@@ -154,13 +178,21 @@ tp_status tp_linear_column_ex(const void *X, const void *const *x_slices, int64_
                 if (!x_slices[j]) return TP_ERR_NULL;
     }
 
+    // Shard strides from the placements: W [N, K] Shard(0) (row blocks); Y
+    // concatenated = [M, P*On] Shard(1) (column blocks), or P shard buffers
+    // stacked = [P*M, On] Shard(0); the bias [N] Shard(0).  X is Replicate.
+    const int64_t w_stride = view_stride(N, K, ldw, TP_SHARD, 0, P);
+    const int64_t y_stride = y_mode == TP_Y_CONCAT ? view_stride(M, P * On, ldy, TP_SHARD, 1, P)
+                                                   : view_stride(P * M, On, ldy, TP_SHARD, 0, P);
+    const int64_t b_stride = view_stride(N, 1, 1, TP_SHARD, 0, P);
+    if (w_stride < 0 || y_stride < 0 || b_stride < 0) return TP_ERR_SHAPE;
     GemmArgs g;
     g.A = X; g.lda = ldx; g.a_shard = 0;
-    g.B = W; g.ldb = ldw; g.b_shard = Ns * ldw;
-    g.C = Y; g.ldc = ldy; g.c_shard = y_mode == TP_Y_CONCAT ? On : M * ldy;
+    g.B = W; g.ldb = ldw; g.b_shard = w_stride;
+    g.C = Y; g.ldc = ldy; g.c_shard = y_stride;
     g.M = M; g.N = On; g.K = K; g.P = P;
     GemmExtra ex{};
-    ex.bias = bias; ex.bias_shard = Ns;
+    ex.bias = bias; ex.bias_shard = b_stride;
     ex.act = swiglu ? ACT_SWIGLU : ACT_NONE; ex.up_off = swiglu ? On : 0;
     ex.x_rows = 0;
     if (x_slices && K > 0) {
@@ -208,6 +240,8 @@ tp_status tp_linear_row_ex(const void *X, int64_t ldx, const void *W, int64_t ld
     if (!extent_ok(M, ldy, mode == TP_ROW_PARTIAL ? P : 1) ||
         !extent_ok(M, N, (int64_t)P * (int64_t)sizeof(float)) || !extent_ok(P, y_slice_stride))
         return TP_ERR_SHAPE;
+    if (mode == TP_ROW_SCATTER && !y_slices && !slice_stride_ok(y_slice_stride, M / P, N, ldy))
+        return TP_ERR_SHAPE;
     if (M == 0 || N == 0) return TP_OK;
     if (y_slices) {
         for (int32_t j = 0; j < P; ++j)
@@ -222,19 +256,30 @@ tp_status tp_linear_row_ex(const void *X, int64_t ldx, const void *W, int64_t ld
 
     const hipStream_t s = (hipStream_t)stream;
     const int64_t Ks = K / P;
+    // Shard strides from the placements: X [M, K] and W [N, K] Shard(1)
+    // (column blocks); the partials Partial() (P [M, N] buffers back to
+    // back, row stride ldy in Y or N in the workspace); the reduce-scatter's
+    // slices Shard(0) of Y (row blocks) unless a slice stride is given.
+    const int64_t x_stride = view_stride(M, K, ldx, TP_SHARD, 1, P);
+    const int64_t w_stride = view_stride(N, K, ldw, TP_SHARD, 1, P);
+    if (x_stride < 0 || w_stride < 0) return TP_ERR_SHAPE;
     GemmArgs g;
-    g.A = X; g.lda = ldx; g.a_shard = Ks;
-    g.B = W; g.ldb = ldw; g.b_shard = Ks;
+    g.A = X; g.lda = ldx; g.a_shard = x_stride;
+    g.B = W; g.ldb = ldw; g.b_shard = w_stride;
     g.M = M; g.N = N; g.K = Ks; g.P = P;
     const int out = dtype == TP_BF16 ? OUT_BF16 : OUT_F32;
 
     if (mode == TP_ROW_PARTIAL) {
-        g.C = Y; g.ldc = ldy; g.c_shard = M * ldy;
+        const int64_t p_stride = view_stride(M, N, ldy, TP_PARTIAL, 0, P);
+        if (p_stride < 0) return TP_ERR_SHAPE;
+        g.C = Y; g.ldc = ldy; g.c_shard = p_stride;
         return hip_status(run_gemm(g, dtype, OUT_F32, nullptr, s));
     }
 
+    const int64_t p_stride = view_stride(M, N, N, TP_PARTIAL, 0, P);
+    if (p_stride < 0) return TP_ERR_SHAPE;
     float *parts = (float *)workspace;
-    g.C = parts; g.ldc = N; g.c_shard = M * N;
+    g.C = parts; g.ldc = N; g.c_shard = p_stride;
 
     if (mode == TP_ROW_FUSED && dtype == TP_BF16 && gemm_skinny_supported(g, nullptr)) {
         FoldArgs f;
@@ -245,13 +290,15 @@ tp_status tp_linear_row_ex(const void *X, int64_t ldx, const void *W, int64_t ld
     }
 
     ReduceArgs r;
-    r.partials = parts; r.shard_stride = M * N; r.ldp = N;
+    r.partials = parts; r.shard_stride = p_stride; r.ldp = N;
     r.Y = Y; r.ldy = ldy; r.M = M; r.N = N; r.P = P;
     r.bias = bias;
     set_out_slices(r, y_slices, P);
     if (mode == TP_ROW_SCATTER) {
+        const int64_t s_stride = view_stride(M, N, ldy, TP_SHARD, 0, P);
+        if (s_stride < 0) return TP_ERR_SHAPE;
         r.slice_rows = M / P;
-        r.slice_stride = y_slice_stride ? y_slice_stride : (M / P) * ldy;
+        r.slice_stride = y_slice_stride ? y_slice_stride : s_stride;
     } else {
         r.slice_rows = M;
         r.slice_stride = 0;
@@ -296,6 +343,8 @@ tp_status tp_shard_reduce_ex(const float *partials, int64_t shard_stride, int64_
     if (scatter != 0 && scatter != 1) return TP_ERR_MODE;
     if (y_slices && !scatter) return TP_ERR_MODE;
     if (scatter && M % P != 0) return TP_ERR_INDIVISIBLE;
+    if (scatter && !y_slices && !slice_stride_ok(y_slice_stride, M / P, N, ldy))
+        return TP_ERR_SHAPE;
     if (M == 0 || N == 0) return TP_OK;
     if (!partials) return TP_ERR_NULL;
     if (y_slices) {
@@ -310,8 +359,11 @@ tp_status tp_shard_reduce_ex(const float *partials, int64_t shard_stride, int64_
     r.bias = bias;
     set_out_slices(r, y_slices, P);
     if (scatter) {
+        // the slices: Shard(0) of Y (row blocks) unless a stride is given
+        const int64_t s_stride = view_stride(M, N, ldy, TP_SHARD, 0, P);
+        if (s_stride < 0) return TP_ERR_SHAPE;
         r.slice_rows = M / P;
-        r.slice_stride = y_slice_stride ? y_slice_stride : (M / P) * ldy;
+        r.slice_stride = y_slice_stride ? y_slice_stride : s_stride;
     } else {
         r.slice_rows = M;
         r.slice_stride = 0;
@@ -343,10 +395,17 @@ tp_status tp_embedding(const int64_t *ids, int64_t T, const void *E, const void 
         return TP_ERR_SHAPE;
     if (T == 0 || D == 0) return TP_OK;
     if (!ids || !Y || (E != nullptr) == (e_shards != nullptr)) return TP_ERR_NULL;
+    // Shard strides from the placements: the table [V, D] Shard(1) (column
+    // blocks of the embedding dim); the output concatenated = [T, D]
+    // Shard(1), or P shard buffers stacked = [P*T, Ds] Shard(0).
+    const int64_t e_stride = E ? view_stride(V, D, lde, TP_SHARD, 1, P) : 0;
+    const int64_t y_stride = y_mode == TP_Y_CONCAT ? view_stride(T, D, ldy, TP_SHARD, 1, P)
+                                                   : view_stride(P * T, Ds, ldy, TP_SHARD, 0, P);
+    if (e_stride < 0 || y_stride < 0) return TP_ERR_SHAPE;
     EmbedArgs e;
     e.ids = ids; e.T = T; e.V = V; e.Ds = Ds; e.P = P;
     e.lde = lde; e.Y = Y; e.ldy = ldy;
-    e.y_shard = y_mode == TP_Y_CONCAT ? Ds : T * ldy;
+    e.y_shard = y_stride;
     e.bad = bad_flag;
     const size_t es = dtype_bytes(dtype);
     for (int j = 0; j < MAX_SLICES; ++j) e.e_shard[j] = nullptr;
@@ -355,7 +414,7 @@ tp_status tp_embedding(const int64_t *ids, int64_t T, const void *E, const void 
             if (!e_shards[i]) return TP_ERR_NULL;
             e.e_shard[i] = e_shards[i];
         } else {
-            e.e_shard[i] = (const char *)E + (size_t)i * Ds * es;
+            e.e_shard[i] = (const char *)E + (size_t)(i * e_stride) * es;
         }
     }
     return hip_status(launch_embedding(e, (int)es, (hipStream_t)stream));

@@ -83,6 +83,11 @@ int main() {
           TP_ERR_INDIVISIBLE);
     CHECK(tp_linear_row_ex(F, 8, F, 8, F, F, nullptr, 12, 0, TP_ROW_PARTIAL, nullptr, 0, 4, 12, 8, 4, TP_BF16,
                            nullptr) == TP_ERR_MODE);
+    // Overlapping reduce-scatter slices (stride below (M/P - 1)*ldy + N).
+    CHECK(tp_linear_row(F, 8, F, 8, F, 12, 23, TP_ROW_SCATTER, F, 1 << 20, 8, 12, 8, 4, TP_BF16, nullptr) ==
+          TP_ERR_SHAPE);
+    CHECK(tp_shard_reduce(static_cast<const float *>(F), 96, 12, F, 12, 11, 1, 4, 12, 4, TP_BF16, nullptr) ==
+          TP_ERR_SHAPE);
     void *yslices[4] = {F, F, F, nullptr};
     CHECK(tp_linear_row_ex(F, 8, F, 8, nullptr, nullptr, yslices, 12, 0, TP_ROW_SCATTER, F, 1 << 20, 4, 12, 8, 4,
                            TP_BF16, nullptr) == TP_ERR_NULL);

@@ -162,6 +162,11 @@ def test_row_errors():
     assert row(P=0) == tl.TP_ERR_SHAPE
     assert row(ldy=11) == tl.TP_ERR_SHAPE
     assert row(ss=-1, mode=tl.TP_ROW_SCATTER) == tl.TP_ERR_SHAPE
+    # slices that would overlap: a nonzero stride below (M/P - 1)*ldy + N
+    assert row(ss=11, mode=tl.TP_ROW_SCATTER) == tl.TP_ERR_SHAPE            # M/P = 1
+    assert row(ss=23, M=8, mode=tl.TP_ROW_SCATTER) == tl.TP_ERR_SHAPE      # M/P = 2
+    assert row(ss=23, M=8, ldy=16, mode=tl.TP_ROW_SCATTER) == tl.TP_ERR_SHAPE
+    assert row(ss=11, mode=tl.TP_ROW_SCATTER, M=0) == tl.TP_OK           # empty: nothing written
     assert row(K=10, ldx=10, ldw=10) == tl.TP_ERR_INDIVISIBLE
     assert row(M=6, mode=tl.TP_ROW_SCATTER) == tl.TP_ERR_INDIVISIBLE
     assert row(dtype=7) == tl.TP_ERR_DTYPE
@@ -188,6 +193,8 @@ def test_reduce_errors():
     assert red(dtype=3) == tl.TP_ERR_DTYPE
     assert red(scatter=2) == tl.TP_ERR_MODE
     assert red(scatter=1, M=6) == tl.TP_ERR_INDIVISIBLE
+    assert red(scatter=1, yss=11) == tl.TP_ERR_SHAPE                     # overlapping slices
+    assert red(scatter=1, yss=23, M=8, ss=96) == tl.TP_ERR_SHAPE
     assert red(M=0) == tl.TP_OK
 
 
@@ -248,9 +255,74 @@ def test_binding_rejects_host_tensors():
         lambda: tl.tp_linear_row_ex(X, W, parts, 4, tl.TP_ROW_PARTIAL),
         lambda: tl.tp_shard_reduce(parts, Y, 4),
         lambda: tl.tp_shard_reduce_ex(parts, Y, 4),
-        lambda: tl.tp_embedding(torch.zeros(4, dtype=torch.int64), Y, 4, E=W),
+        lambda: tl.tp_embedding(torch.zeros(4, dtype=torch.int64), torch.zeros(4, 8, dtype=bf), 4,
+                                E=W),
         lambda: tl.tp_workspace_zero(torch.zeros(16, dtype=torch.uint8)),
     ]
     for c in calls:
         with pytest.raises(ValueError, match="GPU tensor"):
             c()
+
+
+def test_binding_rejects_misshaped_outputs():
+    """The library writes exactly the output the sizes call for; the binding
+    refuses an output tensor of another shape (too few rows, a narrower
+    column view, a wrong block shape) or a slice buffer too small for P
+    strided slices, before any device check or library call."""
+    import torch
+    bf, f32 = torch.bfloat16, torch.float32
+    M, K, N, P = 8, 16, 12, 4
+    X, W = torch.zeros(M, K, dtype=bf), torch.zeros(N, K, dtype=bf)
+    parts = torch.zeros(P, M, N)
+    Y = lambda *s: torch.zeros(*s, dtype=bf)                      # noqa: E731
+    bad = [
+        lambda: tl.tp_linear_column(X, W, Y(M - 1, N), P),
+        lambda: tl.tp_linear_column(X, W, Y(M, N + 4)[:, :N - 1], P),
+        lambda: tl.tp_linear_column(X, W, Y(P, M, N // P - 1), P, tl.TP_Y_SHARDS),
+        lambda: tl.tp_linear_column(X, W, Y(P, M - 1, N // P), P, tl.TP_Y_SHARDS),
+        lambda: tl.tp_linear_column_ex(X, torch.zeros(16, K, dtype=bf), Y(M, 16), P,
+                                       act=tl.TP_ACT_SWIGLU),      # needs [M, 8]
+        lambda: tl.tp_linear_column_ex(X, W, Y(M, N), P, bias=Y(N - 1)),
+        lambda: tl.tp_linear_row(X, W, Y(M - 1, N), P, tl.TP_ROW_SUM),
+        lambda: tl.tp_linear_row(X, W, Y(M, N - 1), P, tl.TP_ROW_FUSED),
+        lambda: tl.tp_linear_row(X, W, torch.zeros(P, M, N - 1), P, tl.TP_ROW_PARTIAL),
+        lambda: tl.tp_linear_row(X, W, torch.zeros(P - 1, M, N), P, tl.TP_ROW_PARTIAL),
+        lambda: tl.tp_linear_row_ex(X, W, Y(M, N), P, bias=Y(N + 1)),
+        # slice 0 of P strided slices: the buffer must reach the last slice
+        lambda: tl.tp_linear_row(X, W, Y(P * 2 * N)[:2 * N].view(2, N), P,
+                                 tl.TP_ROW_SCATTER, y_slice_stride=3 * N),
+        lambda: tl.tp_linear_row(X, W, Y(M // P + 1, N), P, tl.TP_ROW_SCATTER,
+                                 y_slice_stride=3 * N),
+        lambda: tl.tp_shard_reduce(parts, Y(M, N + 1), P),
+        lambda: tl.tp_shard_reduce(parts, Y(M - 1, N), P, scatter=1),
+        lambda: tl.tp_shard_reduce(parts, Y(4 * N)[:2 * N].view(2, N), P, scatter=1,
+                                   y_slice_stride=2 * N),
+        lambda: tl.tp_shard_reduce_ex(parts, Y(M, N), P, bias=Y(N - 1)),
+        lambda: tl.tp_embedding(torch.zeros(5, dtype=torch.int64), Y(4, 16), P, E=Y(10, 16)),
+        lambda: tl.tp_embedding(torch.zeros(5, dtype=torch.int64), Y(5, 12), P, E=Y(10, 16)),
+        lambda: tl.tp_embedding(torch.zeros(5, dtype=torch.int64), Y(P, 5, 3), P, E=Y(10, 16),
+                                y_mode=tl.TP_Y_SHARDS),
+    ]
+    for i, c in enumerate(bad):
+        with pytest.raises(ValueError, match="shape|storage") as e:
+            c()
+        assert "GPU tensor" not in str(e.value), i
+    # correctly shaped host outputs pass the shape checks and reach the
+    # device check (the slice buffer here holds all P slices exactly)
+    ok = [
+        lambda: tl.tp_linear_column(X, W, Y(M, N), P),
+        lambda: tl.tp_linear_row(X, W, Y(P * 3 * N)[:2 * N].view(2, N), P, tl.TP_ROW_SCATTER,
+                                 y_slice_stride=3 * N),
+        lambda: tl.tp_shard_reduce(parts, Y(3 * 2 * N + 2 * N)[:2 * N].view(2, N), P,
+                                   scatter=1, y_slice_stride=2 * N),
+    ]
+    for c in ok:
+        with pytest.raises(ValueError, match="GPU tensor"):
+            c()
+    # an indivisible split is the library's status, also from the binding
+    with pytest.raises(tl.TPError) as e:
+        tl.tp_linear_column(X, torch.zeros(10, K, dtype=bf), Y(M, 10), P)
+    assert e.value.status == tl.TP_ERR_INDIVISIBLE
+    with pytest.raises(tl.TPError) as e:
+        tl.tp_shard_reduce(torch.zeros(P, 6, N, dtype=f32), Y(6, N), P, scatter=1)
+    assert e.value.status == tl.TP_ERR_INDIVISIBLE

@@ -75,11 +75,19 @@ def test_fused_fold_repeat_and_strided_output():
         assert bool(torch.all(buf[:, :8] == -7.0)) and bool(torch.all(buf[:, 8 + N:] == -7.0))
 
 
-@pytest.mark.parametrize("slices", [False, True])
-def test_fused_reduce_scatter(slices):
-    # M/P = 256-row token slices: the reduce-scatter runs as the fused fold;
-    # its slices equal the rows of TP_ROW_SUM bit for bit.
-    M, K, N, P = 2048, 8192, 1024, 8
+@pytest.mark.parametrize("M,K,N,P,slices", [
+    (2048, 8192, 1024, 8, False),
+    (2048, 8192, 1024, 8, True),
+    # P = 1 with a slice allocation: one slice, the whole (ragged) output,
+    # written through the slice table (a regression case: this shape once
+    # took the path that writes through Y, which is NULL with y_slices)
+    (320, 512, 384, 1, True),
+    (320, 512, 384, 1, False),
+])
+def test_fused_reduce_scatter(M, K, N, P, slices):
+    # M/P = 256-row token slices (or one slice): the reduce-scatter runs as
+    # the fused fold; its slices equal the rows of TP_ROW_SUM bit for bit.
+    print(f"fused reduce-scatter M={M} K={K} N={N} P={P} slices={slices}", flush=True)
     gen = torch.Generator(device=DEV)
     gen.manual_seed(11)
     X, W = _rand(gen, (M, K)), _rand(gen, (N, K), 0.02)

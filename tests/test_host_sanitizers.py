@@ -37,6 +37,24 @@ def test_abi_host_code_under_sanitizers(tmp_path):
     assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr
 
 
+@pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not found")
+def test_launch_offsets_follow_layout(tmp_path):
+    """One placement map: the shard offsets each entry point passes to its
+    kernels (recorded by stub launchers) equal tp_shard_layout's views of the
+    layer's placements, for every mode (tests/host/launch_map_driver.cpp)."""
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROOT, "tensor_linear_amd", "csrc"),
+           "-I", "/opt/rocm/include", "-D__HIP_PLATFORM_AMD__"]
+    obj = str(tmp_path / "tplinear.o")
+    _run(["g++", "-std=c++17", "-O1", "-c", os.path.join(ROOT, "tensor_linear_amd", "csrc", "tplinear.cpp"),
+          "-o", obj] + SAN + inc, tmp_path)
+    exe = str(tmp_path / "launch_map_driver")
+    _run(["g++", "-std=c++17", "-O1", os.path.join(HOST, "launch_map_driver.cpp"), obj, "-o", exe] + SAN + inc,
+         tmp_path)
+    r = _run([exe], tmp_path)
+    assert "launch map driver ok" in r.stdout
+    assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr
+
+
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not found")
 def test_oracle_under_sanitizers(tmp_path):
     exe = str(tmp_path / "oracle_driver")
