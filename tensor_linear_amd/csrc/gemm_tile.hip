@@ -4,41 +4,67 @@
 // the [N, K] weight storage, so no transpose is needed).
 //
 // Output tile 256 (M) x 256 (N); 256 threads = 4 waves in a 2x2 grid, each
-// wave owning a 128x128 block = 4x4 v_mfma_f32_32x32x16_bf16 accumulators
-// (256 fp32 registers per lane).  The W tile is the MFMA row operand and the
-// X tile the column operand, so each lane holds 4 consecutive output columns
-// of one row: 16-byte fp32 / 8-byte bf16 stores.
+// wave owning a 128x128 block = 8x8 v_mfma_f32_16x16x32_bf16 accumulators
+// (256 fp32 registers per lane).  The 16x16x32 form and not 32x32x16: at
+// full issue rate with random operands the chip holds about 2.0 GHz under
+// the former and about 1.66 GHz under the latter (the same flops per
+// instruction-cycle; the clock is power-limited), and the results are the
+// same bit for bit.  The W tile is the MFMA row operand and the X tile the
+// column operand, so each lane holds 4 consecutive output columns of one
+// output row.
 //
-// Persistent: one workgroup per CU walks a list of tiles, and the K pipeline
-// runs straight across tile boundaries -- the first K steps of the next tile
-// are loaded while the current tile finishes and writes its outputs -- so no
-// CU sits idle between tiles.  Workgroup b runs on XCD b % 8; the tiles are
-// split into 8 contiguous ranges, one per XCD, and inside a range the 32
-// workgroups of the XCD take consecutive tiles (visited in groups of 8
-// tile-rows, 4 for fp32 partials), so the panels of X and W they share stay
-// in that XCD's L2.
+// Persistent: one workgroup per CU walks a list of tiles and the K pipeline
+// runs straight across tile boundaries.  Workgroup b runs on XCD b % 8; the
+// tiles are split into 8 contiguous ranges, one per XCD, and inside a range
+// the 32 workgroups of the XCD take consecutive tiles (visited in groups of 8
+// tile-rows, 4 for fp32 partials), so the panels of X and W they share stay in
+// that XCD's L2.
 //
-// Global -> LDS: global_load_lds_dwordx4 (16 bytes per lane straight into
-// LDS, no register staging), NST stages of BK columns of K.  One wave
-// instruction fills 1 KB of LDS.  Rows are BK*2 bytes; 16-byte chunk c of row
-// r sits at slot c ^ ((r / RP) % CPR) (RP rows per 256 bytes, CPR chunks per
-// row), so the 16 rows read by one 16-lane group of ds_read_b128 hit 16
-// different 16-byte bank groups.
+// LDS: three X stages and two W stages of K = 64 (5 x 32 KB = 160 KB), rows
+// of 128 bytes (one cache line); 16-byte chunk c of row r at slot
+// c ^ ((r / 2) % 8), so the 16 rows a 16-lane group of ds_read_b128 reads hit
+// 16 different bank groups.  Global -> LDS with global_load_lds_dwordx4 (one
+// 1 KB wave instruction = 8 rows, no register staging).  Each step's 16 loads
+// per wave are spread evenly, 4 per phase: the W half loaded one step ahead
+// has 3-4 phases of lead, the X loaded two steps ahead (the third X stage
+// makes room for it) 5-6 phases -- with two stages of each, a whole step had
+// to be loaded in the two phases after the stage came free.
+//
+// Per step (K = 64 = two 32-wide substeps), 4 phases of 32 MFMAs (16 cycles
+// each): phases 0-1 substep 0 (W blocks 0-3, then 4-7, each against X blocks
+// 0-7), phases 2-3 substep 1.  One barrier per step, before phase 3; the
+// fragment reads are placed so that each is read well before its first use
+// and no fragment register is overwritten before its last:
+//   phase 0: substep-0 W4-7 of this step, substep-1 X0-3
+//   phase 1: substep-1 W0, X4-7, W1-3
+//   phase 2: substep-1 W4-7
+//   (barrier: step it+1 has landed; every wave is done with step it's stages)
+//   phase 3: step it+1 substep-0 W0, X0-7, W1-3
+// DMA loads: phase 0 the second W half of step it+1, phases 1-2 X of step
+// it+2, phase 3 the first W half of step it+2.
 //
 // Each tile's first MFMA of every accumulator block takes a zero C operand,
 // so no accumulator registers are cleared between tiles.
 //
-// Edges: rows past M or N are clamped to the last valid row (their results
-// are not stored).  K must be a positive multiple of BK.  Tiles entirely
-// inside M x N store without per-store bounds tests.
+// Epilogue: 32 output rows x 64 columns at a time go through this wave's part
+// of the X stage the tile's last barrier freed (its own 1 KB DMA chunks, which
+// only its own later loads overwrite): written in the MFMA layout, read back
+// row-contiguous, so a bf16 row leaves as one full 128-byte line and an fp32
+// row as two.  Stores are non-temporal (measured faster than cached stores
+// for every shape: the burst of all CUs' tiles would fill the L2 with dirty
+// lines the next loads wait behind).
+//
+// Edges: rows past M or N are clamped to the last valid row (their results are
+// not stored).  K must be a positive multiple of 64.  Tiles entirely inside
+// M x N store without per-store bounds tests.
 //
 // Epilogue options (template EPI): EPI_BIAS adds the column bias (Shard(0),
 // "Module 并行：实现 DP/TP/CP/PP 组合", "Linear 实现解析") to the fp32
 // accumulators before rounding; EPI_SWIGLU is the gated unit of a fused
 // gate+up column layer: the W tile's 256 rows are 128 gate rows and the 128
-// up rows of the same hidden units, placed so that each wave's MFMA blocks
-// 0-1 hold gate and blocks 2-3 the matching up features in the same lanes;
-// the output tile is 256 tokens x 128 hidden units, silu(g + bg) * (u + bu).
+// up rows of the same hidden units, placed so that each wave's W blocks 0-3
+// hold gate and blocks 4-7 the matching up features in the same lanes; the
+// output tile is 256 tokens x 128 hidden units, silu(g + bg) * (u + bu).
 // XG: the X rows come from token slices in separate allocations (the
 // all-gather of the sequence-parallel layout read in place); a tile never
 // spans two slices, so only its base pointer changes.
@@ -49,14 +75,12 @@ namespace tpl {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_PTR(T) __attribute__((address_space(3))) T *
 
-constexpr int TB = 256;  // tile edge in M and N (W rows)
-constexpr int TT = 256;  // threads
+constexpr int TB = 256;   // tile edge in M and N (W rows)
+constexpr int TT = 256;   // threads
 
 enum { EPI_NONE = 0, EPI_BIAS = 1, EPI_SWIGLU = 2 };
 
@@ -97,40 +121,33 @@ __device__ __forceinline__ int tile_of(const TileSched &ts, int q) {
     return t < ts.T ? t : -1;
 }
 
-template <int BK, int NST, int OUT, int EPI, bool XG>
+template <int OUT, int EPI, bool XG>
 __global__ __attribute__((amdgpu_flat_work_group_size(TT, TT), amdgpu_waves_per_eu(1, 1)))
 void gemm_tile_kernel(GemmArgs g, TileSched ts, int vec_store, GemmExtra ex) {
     constexpr bool SWIGLU = EPI == EPI_SWIGLU;
     constexpr int TBN = SWIGLU ? TB / 2 : TB;   // output columns per tile
-    constexpr int ROWB = BK * 2;          // LDS bytes per tile row
-    constexpr int CPR = BK / 8;           // 16-byte chunks per row
-    constexpr int RP = 256 / ROWB;        // rows per 256 bytes
-    constexpr int OPB = TB * ROWB;        // one operand tile
-    constexpr int STAGE = 2 * OPB;        // X tile + W tile
-    constexpr int RPI = 1024 / ROWB;      // rows per 1 KB load instruction
-    constexpr int LPW = OPB / 1024 / 4;   // load instructions per operand per wave
-    constexpr int KS = BK / 16;           // MFMA k-steps per stage
-    constexpr int EPI_ROWB = 32 * 4 + 16;   // one fp32 row of a 32x32 block, padded
-    constexpr int EPI_WAVE = 32 * EPI_ROWB; // per-wave staging area
-    static_assert(NST * STAGE + 4 * EPI_WAVE <= 160 * 1024, "LDS");
-    __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE + 4 * EPI_WAVE];
+    constexpr int ROWB = 128;                   // LDS bytes per tile row (K = 64)
+    constexpr int OPB = TB * ROWB;              // one operand stage, 32 KB
+    constexpr int LPW = 8;                      // 1 KB loads per operand per wave per step
+    constexpr int W_BASE = 3 * OPB;             // three X stages, then two W stages
+    __shared__ __attribute__((aligned(1024))) char smem[5 * OPB];
     LDS_PTR(char) lds = (LDS_PTR(char))smem;
+    const uint32_t lds_u = (uint32_t)(uintptr_t)lds;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
 
-    // Number of tiles this workgroup owns.
     int ntiles = 0;
     while (tile_of(ts, ntiles) >= 0) ++ntiles;
-    const int nk = (int)(g.K / BK);
+    const int nk = (int)(g.K / 64);
     if (ntiles == 0) return;
     const int total = ntiles * nk;
 
-    // ---- prefetch cursor (runs NST-1 steps ahead of the compute cursor).
-    // Per-lane load offsets depend on the tile (row clamping), so they are
-    // rebuilt whenever the cursor enters a new tile.
+    // ---- load cursor: the step whose operands are being loaded.  Per-lane
+    // load offsets depend on the tile (row clamping), so they are rebuilt
+    // whenever the cursor enters a new tile.
     int pq = 0, pkt = 0;
     const char *pa = nullptr, *pb = nullptr;
     uint32_t aoff[LPW], boff[LPW];
@@ -150,18 +167,18 @@ void gemm_tile_kernel(GemmArgs g, TileSched ts, int vec_store, GemmExtra ex) {
         const int b_rows = (int)min<int64_t>(g.N - n0, TBN);
 #pragma unroll
         for (int j = 0; j < LPW; ++j) {
-            const int r = (j * 4 + wave) * RPI + lane / CPR;
-            const int chunk = (lane % CPR) ^ ((r / RP) % CPR);
+            const int r = (j * 4 + wave) * 8 + lane / 8;
+            const int chunk = (lane % 8) ^ ((r / 2) % 8);
             const int ra = r < a_rows ? r : a_rows - 1;
             int64_t wrow;
             if (SWIGLU) {
-                // LDS row r feeds wave r / 128, MFMA block (r / 32) % 4:
-                // blocks 0-1 gate rows, blocks 2-3 the up rows of the same
+                // LDS row r feeds wave half r / 128, W block (r / 16) % 8:
+                // blocks 0-3 gate rows, blocks 4-7 the up rows of the same
                 // 64 hidden units.
-                const int blk = (r >> 5) & 3;
-                int h = ((r >> 7) << 6) + ((blk & 1) << 5) + (r & 31);
+                const int blk = (r >> 4) & 7;
+                int h = ((r >> 7) << 6) + ((blk & 3) << 4) + (r & 15);
                 h = h < b_rows ? h : b_rows - 1;
-                wrow = h + (blk >= 2 ? ex.up_off : 0);
+                wrow = h + (blk >= 4 ? ex.up_off : 0);
             } else {
                 wrow = r < b_rows ? r : b_rows - 1;
             }
@@ -169,24 +186,6 @@ void gemm_tile_kernel(GemmArgs g, TileSched ts, int vec_store, GemmExtra ex) {
             boff[j] = (uint32_t)((wrow * g.ldb + chunk * 8) * 2);
         }
     };
-    // Issue loads [j0, j1) of the cursor's step into `stage` (branch-free;
-    // loads 0..LPW-1 fill the X tile, LPW..2*LPW-1 the W tile).
-    auto issue_part = [&](int stage, int j0, int j1) {
-        LDS_PTR(char) dst = lds + stage * STAGE;
-        const int64_t kb = (int64_t)pkt * BK * 2;
-#pragma unroll
-        for (int j = 0; j < 2 * LPW; ++j) {
-            if (j < j0 || j >= j1) continue;
-            if (j < LPW)
-                __builtin_amdgcn_global_load_lds((const void *)(pa + kb + aoff[j]),
-                                                 (LDS_PTR(void))(dst + (j * 4 + wave) * 1024), 16, 0, 0);
-            else
-                __builtin_amdgcn_global_load_lds(
-                    (const void *)(pb + kb + boff[j - LPW]),
-                    (LDS_PTR(void))(dst + OPB + ((j - LPW) * 4 + wave) * 1024), 16, 0, 0);
-        }
-    };
-    auto issue_step = [&](int stage) { issue_part(stage, 0, 2 * LPW); };
     // Advance the cursor one step.  Past the last step it stays there, so
     // later issues reload the last step into stages that are not read again.
     auto advance = [&]() {
@@ -198,248 +197,244 @@ void gemm_tile_kernel(GemmArgs g, TileSched ts, int vec_store, GemmExtra ex) {
             }
         }
     };
-
-    // With two stages the loads of a step are split in halves: the X half is
-    // issued in the last phase of the step two before it (its stage is free
-    // once that step's barrier has passed), the W half in phase 0 of the step
-    // before it.  Spreading them over two phases keeps the vector memory
-    // queue from backing up into the MFMA issue.  With more stages a whole
-    // step is issued in phase 0, NST-1 steps ahead.
-    enter_tile(0);
-    if (NST == 2) {
-        issue_step(0);
-        advance();
-        issue_part(1, 0, LPW);
-    } else {
-#pragma unroll
-        for (int s = 0; s < NST - 1; ++s) {
-            issue_step(s);
-            advance();
-        }
-    }
-
-    // Fragment addressing: a 32x32x16 operand fragment is 32 rows x 16 k;
-    // lane reads row lane%32, k-chunk 2*ks + lane/32.
-    const int frow = lane & 31;
-    const int fhalf = lane >> 5;
-    const int fx = (frow / RP) % CPR;
-    const int wrow_off = (wn * 128 + frow) * ROWB;
-    const int xrow_off = (wm * 128 + frow) * ROWB;
-    auto read_frags = [&](bf16x8 (&wd)[4], bf16x8 (&xd)[4], LDS_PTR(char) st, int ks) {
-        const int slot = ((2 * ks + fhalf) ^ fx) << 4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) wd[i] = *(LDS_PTR(bf16x8))(st + OPB + wrow_off + i * 32 * ROWB + slot);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) xd[j] = *(LDS_PTR(bf16x8))(st + xrow_off + j * 32 * ROWB + slot);
+    // One 1 KB DMA load: 16 bytes per lane from base + voff into LDS at
+    // lds_addr + 16 * lane.  Issued as an instruction the compiler does not
+    // track: its own wait analysis cannot tell which stage a DMA writes and
+    // would drain every load in flight before the next LDS read; the waits
+    // this pipeline needs are written out below.
+    auto dma = [&](const char *base, uint32_t voff, uint32_t lds_addr) __attribute__((always_inline)) {
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                     :: "v"(voff), "s"(base), "s"(lds_addr) : "memory", "m0");
+    };
+    auto load_x = [&](int slot, int j) __attribute__((always_inline)) {
+        dma(pa + (int64_t)pkt * 128, aoff[j], lds_u + slot * OPB + (j * 4 + wave) * 1024);
+    };
+    auto load_w = [&](int slot, int j) __attribute__((always_inline)) {
+        dma(pb + (int64_t)pkt * 128, boff[j], lds_u + W_BASE + slot * OPB + (j * 4 + wave) * 1024);
     };
 
-    // Step 0's data, then its first fragments.
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPW * (NST - 2)) : "memory");
-    __syncthreads();
-    bf16x8 wf[2][4], xf[2][4];
-    read_frags(wf[0], xf[0], lds, 0);
+    // Prologue: X and W of step 0, X of step 1, the first W half of step 1.
+    enter_tile(0);
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) load_x(0, j);
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) load_w(0, j);
+    advance();
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) load_x(1, j);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) load_w(1, j);
+    asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    asm volatile("s_barrier" ::: "memory");
 
-    // Per K step (KS phases of 16 MFMAs, with the 8 fragment reads after the
-    // first 8 MFMAs and the phase's global->LDS loads after every other MFMA
-    // -- one wave per SIMD issues in order, so memory instructions issued back
-    // to back would stall the wave while its MFMA pipe runs dry):
-    //   phase 0       MFMAs of k-step 0; reads of k-step 1; the loads of the
-    //                 step NST-1 ahead (into the stage freed last step);
-    //   phase ks      MFMAs of k-step ks; reads of k-step ks+1;
-    //   (barrier)     the next step's stage has landed and every wave is done
-    //                 reading this step's stage;
-    //   phase KS-1    MFMAs of the last k-step; reads of the next step's
-    //                 k-step 0, so its LDS latency is hidden too.
+    // Fragments: a 16x16x32 operand fragment is 16 rows x 32 k; lane reads
+    // row lane%16 of its block, 16-byte k-chunk 4*h + lane/16 of substep h.
+    // acc[i][j]: W block i (output columns 16i..), X block j (output rows
+    // 16j..) of the wave's 128x128 block.
+    const int frow = lane & 15;
+    const int fq = lane >> 4;
+    const int fx = (frow / 2) % 8;
+    const uint32_t wrow_off = (wn * 128 + frow) * ROWB;
+    const uint32_t xrow_off = (wm * 128 + frow) * ROWB;
+    // fragment f: 0..7 W blocks, 8..15 X blocks; substep h
+    auto frag_addr = [&](uint32_t xbase, uint32_t wbase, int f, int h) -> uint32_t {
+        const uint32_t slot = (uint32_t)(((4 * h + fq) ^ fx) << 4);
+        if (f < 8) return wbase + wrow_off + f * 16 * ROWB + slot;
+        return xbase + xrow_off + (f - 8) * 16 * ROWB + slot;
+    };
+    bf16x8 fr[2][16];   // [substep][fragment]
+    auto read_frag = [&](int h, int f, uint32_t addr) __attribute__((always_inline)) {
+        fr[h][f] = *(LDS_PTR(bf16x8))(lds + addr);
+    };
+#pragma unroll
+    for (int f = 0; f < 16; ++f) read_frag(0, f, frag_addr(0, W_BASE, f, 0));
+
     int it = 0;
-    bool drained = true;  // no epilogue store is in flight
+    int xs = 0, ws = 0;       // X stage it % 3, W stage it % 2
+    bool drained = true;      // no epilogue store is in flight
     for (int q = 0; q < ntiles; ++q) {
-        f32x16 acc[4][4];
-
+        f32x4 acc[8][8];
         auto kstep = [&](auto first) __attribute__((always_inline)) {
             constexpr bool FIRST = decltype(first)::value;
-            LDS_PTR(char) st = lds + (it % NST) * STAGE;
-            LDS_PTR(char) st_next = lds + ((it + 1) % NST) * STAGE;
+            const int xs1 = xs == 2 ? 0 : xs + 1, ws1 = ws ^ 1;     // stages of step it+1
+            const int xs2 = xs1 == 2 ? 0 : xs1 + 1;                 // X stage of step it+2
+            const uint32_t xb = xs * OPB, wb = W_BASE + ws * OPB;
+            const uint32_t xb1 = xs1 * OPB, wb1 = W_BASE + ws1 * OPB;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int cur = ks & 1, nx = cur ^ 1;
-                if (ks == KS - 1) {
-                    // The next step's loads were issued NST-1 steps ago; the
-                    // NST-2 later groups may stay in flight.  After an epilogue
-                    // its stores are in flight too; then wait for everything.
+            for (int ph = 0; ph < 4; ++ph) {
+                if (ph == 3) {
                     __builtin_amdgcn_sched_barrier(0);
-                    if (NST == 2 || !drained)
-                        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                    // Step it+1's operands have landed (X issued in phases
+                    // 1-2 of step it-1, W in phase 3 of it-1 and phase 0 of
+                    // it); the 8 X loads of step it+2 may stay in flight.
+                    // After an epilogue its stores are in flight too, and a
+                    // store may complete before an older load: wait for all.
+                    // lgkmcnt(0): this wave's reads of step it's stages are
+                    // done before anyone's DMA may overwrite them.
+                    if (drained)
+                        asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
                     else
-                        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPW * (NST - 2)) : "memory");
+                        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+                    asm volatile("s_barrier" ::: "memory");
                     drained = true;
-                    __syncthreads();
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                LDS_PTR(char) rd = ks + 1 < KS ? st : st_next;
-                const int rks = ks + 1 < KS ? ks + 1 : 0;
-                const int slot = ((2 * rks + fhalf) ^ fx) << 4;
-                // Loads of this phase: [j0, j1) of the cursor's step.
-                int j0 = 2 * LPW, j1 = 2 * LPW;
-                if (NST == 2) {
-                    if (ks == 0) { j0 = LPW; j1 = 2 * LPW; }      // W half of step it+1
-                    if (ks == KS - 1) { j0 = 0; j1 = LPW; }       // X half of step it+2
-                } else if (ks == 0) {
-                    j0 = 0; j1 = 2 * LPW;                         // all of step it+NST-1
-                }
-                const int lstage = NST == 2 ? (ks == 0 ? (it + 1) % 2 : it % 2) : (it + NST - 1) % NST;
+                const int h = ph >> 1;
 #pragma unroll
-                for (int u = 0; u < 16; ++u) {
+                for (int u = 0; u < 32; ++u) {
                     __builtin_amdgcn_sched_barrier(0);
-                    // Diagonal order: MFMAs 0..3 touch all 8 fragments, so no
-                    // wait on an LDS read comes after the first global->LDS
-                    // load of the phase (the compiler drains every LDS read at
-                    // such a wait once an LDS-writing load is in flight).
-                    const int i = u & 3, j = ((u & 3) + (u >> 2)) & 3;
-                    if (FIRST && ks == 0)   // the tile's first product of each block: C = 0
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][i], xf[cur][j],
-                                                                            f32x16{}, 0, 0, 0);
+                    const int i = (ph & 1) * 4 + (u >> 3), j = u & 7;
+                    if (FIRST && h == 0)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[0][i], fr[0][8 + j], f32x4{}, 0, 0, 0);
                     else
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][i], xf[cur][j],
-                                                                            acc[i][j], 0, 0, 0);
-                    if (u < 8) {
-                        if (u < 4)
-                            wf[nx][u] = *(LDS_PTR(bf16x8))(rd + OPB + wrow_off + u * 32 * ROWB + slot);
-                        else
-                            xf[nx][u - 4] = *(LDS_PTR(bf16x8))(rd + xrow_off + (u - 4) * 32 * ROWB + slot);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[h][i], fr[h][8 + j], acc[i][j], 0, 0, 0);
+                    // reads: every 4th slot in phases 0-1 (8), every 8th in
+                    // phase 2 (4), every other in phase 3 (12)
+                    const int rs = ph == 3 ? 2 : (ph == 2 ? 8 : 4);
+                    const int nrd = ph == 3 ? 12 : (ph == 2 ? 4 : 8);
+                    const bool rd = (u % rs) == 0 && u / rs < nrd;
+                    if (rd) {
+                        const int k = u / rs;
+                        if (ph == 0) {
+                            if (k < 4) read_frag(0, 4 + k, frag_addr(xb, wb, 4 + k, 0));
+                            else read_frag(1, 8 + (k - 4), frag_addr(xb, wb, 8 + (k - 4), 1));
+                        } else if (ph == 1) {
+                            const int f = k == 0 ? 0 : (k <= 4 ? 8 + 4 + (k - 1) : k - 4);
+                            read_frag(1, f, frag_addr(xb, wb, f, 1));
+                        } else if (ph == 2) {
+                            read_frag(1, 4 + k, frag_addr(xb, wb, 4 + k, 1));
+                        } else {
+                            const int f = k == 0 ? 0 : (k <= 8 ? 8 + (k - 1) : k - 8);
+                            read_frag(0, f, frag_addr(xb1, wb1, f, 0));
+                        }
                     }
-                    // Global->LDS loads after every other MFMA (slots 1, 3,
-                    // ..., 15; two per slot when a phase has more than 8), so
-                    // each wave leaves the CU's load path a slot between its
-                    // loads: 1.5-2% faster on every GEMM shape measured than
-                    // the same loads in 8 consecutive slots.
-                    const int per = j1 - j0 > 8 ? 2 : 1;
-                    const int ls = (u >> 1) * per;
-                    const int lc = (u & 1) ? per : 0;
-                    const int la = j0 + ls < j1 ? j0 + ls : j1;
-                    const int lb = j0 + ls + lc < j1 ? j0 + ls + lc : j1;
-                    if (la < lb) issue_part(lstage, la, lb);
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
-                    if (u < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);       // DS read
-                    if (lb - la >= 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // VMEM
-                    if (lb - la >= 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                    // DMA loads every 8th slot, between the reads
+                    const int l0 = ph == 3 ? 1 : (ph == 2 ? 4 : 2);
+                    const bool ld = u >= l0 && (u - l0) % 8 == 0;
+                    if (ld) {
+                        const int l = (u - l0) / 8;   // 0..3
+                        if (ph == 0) load_w(ws1, 4 + l);        // second W half of step it+1
+                        else if (ph == 1) load_x(xs2, l);       // X of step it+2
+                        else if (ph == 2) load_x(xs2, 4 + l);
+                        else load_w(ws, l);                     // first W half of step it+2
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                    if (rd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
                 }
-                if (NST == 2 && ks == 0) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    advance();
-                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (ph == 0) advance();
             }
             __builtin_amdgcn_sched_barrier(0);
-            if (NST != 2) advance();
+            xs = xs1;
+            ws = ws1;
         };
         kstep(std::true_type{});
         ++it;
         for (int kt = 1; kt < nk; ++kt, ++it) kstep(std::false_type{});
 
-        // ---- epilogue.  32x32 D layout with W rows as the row operand:
-        // lane holds m = lane%32 and, for r4 = 0..3, the 4 columns
-        // n = 8*r4 + 4*(lane/32) + 0..3 in registers 4*r4..4*r4+3.
+        // ---- epilogue.  acc[i][j][r] = C[m = 16j + lane%16][n = 16i +
+        // 4*(lane/16) + r] of the wave's block.  Staging: this wave's 1 KB
+        // chunks w + 4c (c = 0..7) of the X stage step it-1 (the tile's last)
+        // read; staging row r of 256 bytes at chunk r/4, offset (r%4)*256,
+        // 16-byte slot s at s ^ (r % 16): conflict-free for the MFMA-layout
+        // writes (16 rows, one slot) and the row-contiguous reads.
+        __builtin_amdgcn_sched_barrier(0);
         int shard, tm, tn;
         decode_tile(ts, tile_of(ts, q), shard, tm, tn);
-        const int64_t tm0 = (int64_t)tm * TB, tn0 = (int64_t)tn * TBN;
         const int64_t cbase = (int64_t)shard * g.c_shard;
-        if constexpr (EPI == EPI_NONE) {
-            // Each 32x32 block goes through this wave's LDS area: written in its
-            // MFMA layout (lane: row m, four consecutive n), read back
-            // row-contiguous, so a store covers whole 64-byte (bf16) or 128-byte
-            // (fp32) row segments.  One path for all tiles: only stores that
-            // cross M or N fall back to element stores.  The stores are
-            // non-temporal: every CU reaches its epilogue at about the same time,
-            // and streaming the burst past L2 keeps it from filling the L2 with
-            // dirty lines the next loads would have to wait behind.
-            {
-                LDS_PTR(char) ep = lds + NST * STAGE + wave * EPI_WAVE;
-                const int64_t tm_w = tm0 + wm * 128, tn_w = tn0 + wn * 128;
-                constexpr int VW = OUT == OUT_BF16 ? 8 : 4;   // values per lane store
-                constexpr int RPP = 64 * VW / 32;              // rows per pass
-                constexpr int ES = OUT == OUT_BF16 ? 2 : 4;    // bytes per value
-                // Tiles inside M x N (all but the last tile row and column) take a
-                // path without per-store bounds tests: one per-lane byte offset
-                // and a uniform base per store.
-                const bool interior = vec_store && tm0 + TB <= g.M && tn0 + TB <= g.N &&
-                                      (int64_t)RPP * g.ldc * ES < (1ll << 31);
-                if (interior) {
-                    const uint32_t lane_off =
-                        (uint32_t)(((int64_t)(lane / (32 / VW)) * g.ldc + VW * (lane % (32 / VW))) * ES);
-                    char *wbase = (char *)g.C + (cbase + tm_w * g.ldc + tn_w) * ES;
-    #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-    #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            __builtin_amdgcn_sched_barrier(0);
-    #pragma unroll
-                            for (int r4 = 0; r4 < 4; ++r4) {
-                                const f32x4 v = {acc[i][j][4 * r4], acc[i][j][4 * r4 + 1],
-                                                 acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]};
-                                *(LDS_PTR(f32x4))(ep + frow * EPI_ROWB + (8 * r4 + 4 * fhalf) * 4) = v;
+        const int es = xs == 0 ? 2 : xs - 1;
+        LDS_PTR(char) ep = lds + es * OPB + wave * 1024;
+        auto st_addr = [&](int r, int s) -> LDS_PTR(char) {
+            return ep + (r >> 2) * 4096 + (r & 3) * 256 + ((s ^ (r & 15)) << 4);
+        };
+        if constexpr (!SWIGLU) {
+            constexpr int ES = OUT == OUT_BF16 ? 2 : 4;
+            const int64_t tm_w = (int64_t)tm * TB + wm * 128, tn_w = (int64_t)tn * TB + wn * 128;
+            const bool interior = vec_store && (int64_t)tm * TB + TB <= g.M &&
+                                  (int64_t)tn * TB + TB <= g.N && (int64_t)32 * g.ldc * ES < (1ll << 31);
+            // interior stores: uniform row base + one per-lane offset; LPR
+            // lanes of 16 bytes per row (8 for bf16: one 128-byte line)
+            constexpr int LPR = OUT == OUT_BF16 ? 8 : 16;
+            const uint32_t lane_off = (uint32_t)((lane / LPR) * g.ldc * ES + (lane % LPR) * 16);
+            const bool has_bias = EPI == EPI_BIAS && ex.bias != nullptr;
+            const __bf16 *bias = has_bias ? (const __bf16 *)ex.bias + (int64_t)shard * ex.bias_shard : nullptr;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {          // output rows 32j.. of the wave
+#pragma unroll
+                for (int ip = 0; ip < 2; ++ip) {   // output columns 64ip.. of the wave
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+                        for (int bi = 0; bi < 4; ++bi)
+                            *(LDS_PTR(f32x4))st_addr(bj * 16 + frow, bi * 4 + fq) = acc[4 * ip + bi][2 * j + bj];
+                    const int64_t ncol = tn_w + ip * 64;
+                    if (OUT == OUT_BF16) {
+                        // lane: row p*8 + lane/8, 8 columns from 8*(lane%8)
+                        const int c8 = lane & 7;
+                        float bv[8];
+                        if (has_bias) {
+                            const int64_t n = ncol + c8 * 8;
+                            if (n + 7 < g.N) {
+                                const bf16x8 b8 = *(const bf16x8 *)(bias + n);
+#pragma unroll
+                                for (int e = 0; e < 8; ++e) bv[e] = (float)b8[e];
+                            } else {
+#pragma unroll
+                                for (int e = 0; e < 8; ++e) bv[e] = n + e < g.N ? (float)bias[n + e] : 0.0f;
                             }
-    #pragma unroll
-                            for (int pp = 0; pp < 32 / RPP; ++pp) {
-                                const int r = pp * RPP + lane / (32 / VW), c = VW * (lane % (32 / VW));
-                                float vv[VW];
-    #pragma unroll
-                                for (int h = 0; h < VW / 4; ++h) {
-                                    const f32x4 a4 = *(LDS_PTR(f32x4))(ep + r * EPI_ROWB + (c + 4 * h) * 4);
-                                    vv[4 * h] = a4[0]; vv[4 * h + 1] = a4[1]; vv[4 * h + 2] = a4[2]; vv[4 * h + 3] = a4[3];
-                                }
-                                char *bp = wbase + ((int64_t)(j * 32 + pp * RPP) * g.ldc + i * 32) * ES + lane_off;
-                                if (OUT == OUT_BF16) {
-                                    bf16x8 hv;
-    #pragma unroll
-                                    for (int e = 0; e < 8; ++e) hv[e] = (__bf16)vv[e];
-                                    __builtin_nontemporal_store(hv, (bf16x8 *)bp);
-                                } else {
-                                    __builtin_nontemporal_store(f32x4{vv[0], vv[1], vv[2], vv[3]}, (f32x4 *)bp);
+                        }
+#pragma unroll
+                        for (int p = 0; p < 4; ++p) {
+                            const int rr = p * 8 + (lane >> 3);
+                            const f32x4 a0 = *(LDS_PTR(f32x4))st_addr(rr, 2 * c8);
+                            const f32x4 a1 = *(LDS_PTR(f32x4))st_addr(rr, 2 * c8 + 1);
+                            float v[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+                            if (has_bias) {
+#pragma unroll
+                                for (int e = 0; e < 8; ++e) v[e] = v[e] + bv[e];
+                            }
+                            bf16x8 hv;
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) hv[e] = (__bf16)v[e];
+                            const int64_t mrow = tm_w + j * 32 + p * 8;
+                            if (interior) {
+                                char *rb = (char *)g.C + (cbase + mrow * g.ldc + ncol) * 2;
+                                __builtin_nontemporal_store(hv, (bf16x8 *)(rb + lane_off));
+                            } else {
+                                const int64_t m = mrow + (lane >> 3), n = ncol + c8 * 8;
+                                if (m < g.M) {
+                                    __bf16 *dst = (__bf16 *)g.C + cbase + m * g.ldc + n;
+                                    if (vec_store && n + 8 <= g.N) {
+                                        __builtin_nontemporal_store(hv, (bf16x8 *)dst);
+                                    } else {
+#pragma unroll
+                                        for (int e = 0; e < 8; ++e)
+                                            if (n + e < g.N) dst[e] = hv[e];
+                                    }
                                 }
                             }
                         }
-                    }
-                } else {
-    #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-    #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            __builtin_amdgcn_sched_barrier(0);
-    #pragma unroll
-                            for (int r4 = 0; r4 < 4; ++r4) {
-                                const f32x4 v = {acc[i][j][4 * r4], acc[i][j][4 * r4 + 1],
-                                                 acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]};
-                                *(LDS_PTR(f32x4))(ep + frow * EPI_ROWB + (8 * r4 + 4 * fhalf) * 4) = v;
-                            }
-                            const int64_t bm = tm_w + j * 32, bn = tn_w + i * 32;
-    #pragma unroll
-                            for (int pp = 0; pp < 32 / RPP; ++pp) {
-                                const int r = pp * RPP + lane / (32 / VW), c = VW * (lane % (32 / VW));
-                                const int64_t m = bm + r, n = bn + c;
-                                float vv[VW];
-    #pragma unroll
-                                for (int h = 0; h < VW / 4; ++h) {
-                                    const f32x4 a4 = *(LDS_PTR(f32x4))(ep + r * EPI_ROWB + (c + 4 * h) * 4);
-                                    vv[4 * h] = a4[0]; vv[4 * h + 1] = a4[1]; vv[4 * h + 2] = a4[2]; vv[4 * h + 3] = a4[3];
-                                }
+                    } else {
+                        // lane: row p*4 + lane/16, 4 columns from 4*(lane%16)
+#pragma unroll
+                        for (int p = 0; p < 8; ++p) {
+                            const int rr = p * 4 + (lane >> 4), sl = lane & 15;
+                            const f32x4 a = *(LDS_PTR(f32x4))st_addr(rr, sl);
+                            const int64_t mrow = tm_w + j * 32 + p * 4;
+                            if (interior) {
+                                char *rb = (char *)g.C + (cbase + mrow * g.ldc + ncol) * 4;
+                                __builtin_nontemporal_store(a, (f32x4 *)(rb + lane_off));
+                            } else {
+                                const int64_t m = mrow + (lane >> 4), n = ncol + sl * 4;
                                 if (m < g.M) {
-                                    const int64_t o = cbase + m * g.ldc + n;
-                                    if (vec_store && n + VW <= g.N) {
-                                        if (OUT == OUT_BF16) {
-                                            bf16x8 hv;
-    #pragma unroll
-                                            for (int e = 0; e < 8; ++e) hv[e] = (__bf16)vv[e];
-                                            __builtin_nontemporal_store(hv, (bf16x8 *)((__bf16 *)g.C + o));
-                                        } else {
-                                            __builtin_nontemporal_store(f32x4{vv[0], vv[1], vv[2], vv[3]},
-                                                                        (f32x4 *)((float *)g.C + o));
-                                        }
+                                    float *dst = (float *)g.C + cbase + m * g.ldc + n;
+                                    if (vec_store && n + 4 <= g.N) {
+                                        __builtin_nontemporal_store(a, (f32x4 *)dst);
                                     } else {
-    #pragma unroll
-                                        for (int e = 0; e < VW; ++e) {
-                                            if (n + e < g.N) {
-                                                if (OUT == OUT_BF16) ((__bf16 *)g.C)[o + e] = (__bf16)vv[e];
-                                                else ((float *)g.C)[o + e] = vv[e];
-                                            }
-                                        }
+#pragma unroll
+                                        for (int e = 0; e < 4; ++e)
+                                            if (n + e < g.N) dst[e] = a[e];
                                     }
                                 }
                             }
@@ -448,124 +443,78 @@ void gemm_tile_kernel(GemmArgs g, TileSched ts, int vec_store, GemmExtra ex) {
                 }
             }
         } else {
-            // With a bias or the gated unit (bf16 output): each 32x32 block
-            // is staged through LDS as above and read back row-contiguous, a
-            // lane holding 8 consecutive columns of a row; the bias and the
-            // activation are applied there, in VGPRs.  For the gated unit the
-            // gate block and then its up block go through the staging area,
-            // so both values of an output meet in the same lane.
-            static_assert(OUT == OUT_BF16, "epilogue options write bf16");
-            LDS_PTR(char) ep = lds + NST * STAGE + wave * EPI_WAVE;
-            constexpr int NI = SWIGLU ? 2 : 4;      // output column blocks per wave
-            constexpr int NH = SWIGLU ? 2 : 1;      // bias vectors per block (gate, up)
-            const int64_t tm_w = tm0 + wm * 128, tn_w = tn0 + wn * (TBN / 2);
-            const int lr = lane >> 2, lc = 8 * (lane & 3);  // row within a 16-row pass, first column
+            // Gated unit: per X block j (16 output rows), the wave's 4 gate
+            // blocks (hidden units 16i..) and 4 up blocks (the same units)
+            // go through the staging area as one 16-row x 128-column fp32
+            // block (gate in slots 0-15, up in 16-31 of 512-byte rows; row r
+            // at chunk r/2, offset (r%2)*512, slot s at s ^ (r % 16)); each
+            // lane then reads 8 gate and 8 up values of one row.
+            static_assert(OUT == OUT_BF16, "the gated unit writes bf16");
+            auto sw_addr = [&](int r, int s) -> LDS_PTR(char) {
+                return ep + (r >> 1) * 4096 + (r & 1) * 512 + ((s ^ (r & 15)) << 4);
+            };
+            const int64_t tm_w = (int64_t)tm * TB + wm * 128, tn_w = (int64_t)tn * TBN + wn * 64;
+            const bool interior = vec_store && (int64_t)tm * TB + TB <= g.M && (int64_t)tn * TBN + TBN <= g.N;
             const bool has_bias = ex.bias != nullptr;
-            bf16x8 bvec[NI][NH];
+            const int c8 = lane & 7;                       // 8 hidden units from 8*c8
+            float bg[8], bu[8];
             if (has_bias) {
                 const __bf16 *bb = (const __bf16 *)ex.bias + (int64_t)shard * ex.bias_shard;
+                const int64_t n = tn_w + c8 * 8;
 #pragma unroll
-                for (int i = 0; i < NI; ++i) {
-#pragma unroll
-                    for (int h = 0; h < NH; ++h) {
-                        const int64_t c = tn_w + i * 32 + lc;
-                        const __bf16 *src = bb + (h ? ex.up_off : 0) + c;
-                        if (c + 7 < g.N) {
-                            bvec[i][h] = *(const bf16x8 *)src;
-                        } else {
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) bvec[i][h][e] = c + e < g.N ? src[e] : (__bf16)0.0f;
-                        }
-                    }
+                for (int e = 0; e < 8; ++e) {
+                    bg[e] = n + e < g.N ? (float)bb[n + e] : 0.0f;
+                    bu[e] = n + e < g.N ? (float)bb[ex.up_off + n + e] : 0.0f;
                 }
             }
-            auto stage = [&](const f32x16 &a) __attribute__((always_inline)) {
 #pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const f32x4 v = {a[4 * r4], a[4 * r4 + 1], a[4 * r4 + 2], a[4 * r4 + 3]};
-                    *(LDS_PTR(f32x4))(ep + frow * EPI_ROWB + (8 * r4 + 4 * fhalf) * 4) = v;
-                }
-            };
-            auto readback = [&](float (&v)[2][8]) __attribute__((always_inline)) {
+            for (int j = 0; j < 8; ++j) {
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int pp = 0; pp < 2; ++pp) {
-                    LDS_PTR(char) rp = ep + (pp * 16 + lr) * EPI_ROWB + lc * 4;
-                    const f32x4 a0 = *(LDS_PTR(f32x4))rp, a1 = *(LDS_PTR(f32x4))(rp + 16);
+                for (int i = 0; i < 8; ++i) *(LDS_PTR(f32x4))sw_addr(frow, i * 4 + fq) = acc[i][j];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) { v[pp][e] = a0[e]; v[pp][4 + e] = a1[e]; }
-                }
-            };
-            const bool interior = vec_store && tm0 + TB <= g.M && tn0 + TBN <= g.N;
+                for (int p = 0; p < 2; ++p) {
+                    const int rr = p * 8 + (lane >> 3);
+                    const f32x4 g0 = *(LDS_PTR(f32x4))sw_addr(rr, 2 * c8);
+                    const f32x4 g1 = *(LDS_PTR(f32x4))sw_addr(rr, 2 * c8 + 1);
+                    const f32x4 u0 = *(LDS_PTR(f32x4))sw_addr(rr, 16 + 2 * c8);
+                    const f32x4 u1 = *(LDS_PTR(f32x4))sw_addr(rr, 16 + 2 * c8 + 1);
+                    const float gv[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+                    const float uv[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+                    bf16x8 hv;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-#pragma unroll
-                for (int i = 0; i < NI; ++i) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    float v[2][8];
-                    stage(acc[i][j]);
-                    readback(v);
-                    if (SWIGLU) {
-                        float u[2][8];
-                        stage(acc[i + 2][j]);
-                        readback(u);
-#pragma unroll
-                        for (int pp = 0; pp < 2; ++pp)
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) {
-                                float gv = v[pp][e], uv = u[pp][e];
-                                if (has_bias) {
-                                    gv = gv + (float)bvec[i][0][e];
-                                    uv = uv + (float)bvec[i][NH - 1][e];
-                                }
-                                v[pp][e] = silu_f32(gv) * uv;
-                            }
-                    } else if (has_bias) {
-#pragma unroll
-                        for (int pp = 0; pp < 2; ++pp)
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) v[pp][e] = v[pp][e] + (float)bvec[i][0][e];
+                    for (int e = 0; e < 8; ++e) {
+                        float gg = gv[e], uu = uv[e];
+                        if (has_bias) {
+                            gg = gg + bg[e];
+                            uu = uu + bu[e];
+                        }
+                        hv[e] = (__bf16)(silu_f32(gg) * uu);
                     }
-#pragma unroll
-                    for (int pp = 0; pp < 2; ++pp) {
-                        const int64_t m = tm_w + j * 32 + pp * 16 + lr, n = tn_w + i * 32 + lc;
-                        bf16x8 hv;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) hv[e] = (__bf16)v[pp][e];
-                        __bf16 *dst = (__bf16 *)g.C + cbase + m * g.ldc + n;
-                        if (interior) {
+                    const int64_t m = tm_w + j * 16 + rr, n = tn_w + c8 * 8;
+                    __bf16 *dst = (__bf16 *)g.C + cbase + m * g.ldc + n;
+                    if (interior) {
+                        __builtin_nontemporal_store(hv, (bf16x8 *)dst);
+                    } else if (m < g.M) {
+                        if (vec_store && n + 8 <= g.N) {
                             __builtin_nontemporal_store(hv, (bf16x8 *)dst);
-                        } else if (m < g.M) {
-                            if (vec_store && n + 8 <= g.N) {
-                                __builtin_nontemporal_store(hv, (bf16x8 *)dst);
-                            } else {
+                        } else {
 #pragma unroll
-                                for (int e = 0; e < 8; ++e)
-                                    if (n + e < g.N) dst[e] = hv[e];
-                            }
+                            for (int e = 0; e < 8; ++e)
+                                if (n + e < g.N) dst[e] = hv[e];
                         }
                     }
                 }
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
         drained = false;
     }
-    // No global->LDS load may still be writing when the workgroup ends.
+    // No DMA load may still be writing LDS when the workgroup ends.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
-
-
-// K per stage and number of stages (tuning parameters; 2 x 64 and 4 x 32 both
-// use 128 KB of LDS).
-#ifndef TPL_TILE_BK
-#define TPL_TILE_BK 64
-#endif
-#ifndef TPL_TILE_NST
-#define TPL_TILE_NST 2
-#endif
-constexpr int KERNEL_BK = TPL_TILE_BK;
-constexpr int KERNEL_NST = TPL_TILE_NST;
 
 }  // namespace
 
@@ -575,7 +524,7 @@ bool gemm_tile_supported(const GemmArgs &g, const GemmExtra *ex) {
     const int64_t wspan = TB + (ex && ex->act == ACT_SWIGLU ? ex->up_off : 0);
     const bool small_rows = (int64_t)TB * g.lda * 2 < (1ll << 31) &&
                             wspan * g.ldb * 2 < (1ll << 31);
-    bool ok = g.K > 0 && g.K % KERNEL_BK == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 &&
+    bool ok = g.K > 0 && g.K % 64 == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 &&
               g.a_shard % 8 == 0 && g.b_shard % 8 == 0 && aligned16(g.B) && small_rows;
     if (!ex) return ok && aligned16(g.A);
     // Bias: 16-byte loads of 8 values per lane.
@@ -596,7 +545,7 @@ namespace {
 template <int OUT, int EPI, bool XG>
 hipError_t launch_tile_t(const GemmArgs &g, const TileSched &ts, int vec, const GemmExtra &ex,
                          int grid, hipStream_t s) {
-    gemm_tile_kernel<KERNEL_BK, KERNEL_NST, OUT, EPI, XG><<<dim3(grid), dim3(TT), 0, s>>>(g, ts, vec, ex);
+    gemm_tile_kernel<OUT, EPI, XG><<<dim3(grid), dim3(TT), 0, s>>>(g, ts, vec, ex);
     return hipGetLastError();
 }
 
