@@ -324,6 +324,33 @@ tp_status tp_embedding(const int64_t *ids, int64_t T, const void *E,
                        void *Y, int64_t ldy, int32_t y_mode, int32_t P, int32_t dtype,
                        int32_t *bad_flag, void *stream);
 
+/*
+ * tp_linear_row_noalloc -- tp_linear_row for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same computation, modes, arguments and errors,
+ * without the workspace arguments.
+ *
+ * The workspace is a fixed array of TP_NOALLOC_SCRATCH_BYTES that the library
+ * holds on each GPU it runs on (reserved when the library is loaded on that
+ * GPU, kept until the process ends).  The call allocates nothing and calls no
+ * allocating routine; the array's device address on the current device is
+ * looked up once per device, on its first call there.
+ * Limit: tp_row_workspace_bytes(mode, M, N, P) <= TP_NOALLOC_SCRATCH_BYTES,
+ *   else TP_ERR_WORKSPACE before anything is queued (modes and shapes that
+ *   need no workspace -- TP_ROW_PARTIAL, and the fused paths -- are not
+ *   limited).  No part of the array has to start at zero: every partial is
+ *   written before the fold reads it.
+ * Concurrency: all calls on one GPU share that GPU's array and it keeps the
+ *   last call's contents, so calls that may overlap on one GPU (on different
+ *   streams without ordering, or from several threads) race on it and must
+ *   be ordered by the caller.
+ */
+#define TP_NOALLOC_SCRATCH_BYTES (32u << 20)
+tp_status tp_linear_row_noalloc(const void *X, int64_t ldx, const void *W, int64_t ldw,
+                                void *Y, int64_t ldy, int64_t y_slice_stride, int32_t mode,
+                                int64_t M, int64_t N, int64_t K, int32_t P,
+                                int32_t dtype, void *stream);
+
 /* Bytes of workspace tp_linear_row needs for (mode, M, N, P); 0 for
  * TP_ROW_PARTIAL, and for invalid arguments (including P*M*N*4 > 2^60,
  * which tp_linear_row rejects with TP_ERR_SHAPE). */

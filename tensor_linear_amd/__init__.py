@@ -52,7 +52,9 @@ TP_MAX_SHARDS = 64
 
 EXPORTS = ("tp_shard_layout", "tp_linear_column", "tp_linear_row", "tp_shard_reduce",
            "tp_linear_column_ex", "tp_linear_row_ex", "tp_shard_reduce_ex", "tp_embedding",
-           "tp_row_workspace_bytes", "tp_workspace_zero", "tp_status_str", "tp_version")
+           "tp_row_workspace_bytes", "tp_workspace_zero", "tp_status_str", "tp_version",
+           "tp_linear_row_noalloc")
+TP_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class tp_placement(ctypes.Structure):
@@ -92,6 +94,9 @@ def _declare(lib):
     lib.tp_embedding.argtypes = [_ptr, _i64, _ptr, _ptr, _i64, _i64, _i64, _ptr, _i64, _i32,
                                  _i32, _i32, _ptr, _ptr]
     lib.tp_embedding.restype = _i32
+    lib.tp_linear_row_noalloc.argtypes = [_ptr, _i64, _ptr, _i64, _ptr, _i64, _i64, _i32,
+                                          _i64, _i64, _i64, _i32, _i32, _ptr]
+    lib.tp_linear_row_noalloc.restype = _i32
     lib.tp_row_workspace_bytes.argtypes = [_i32, _i64, _i64, _i32]
     lib.tp_row_workspace_bytes.restype = _sz
     lib.tp_workspace_zero.argtypes = [_ptr, _sz, _ptr]
@@ -321,6 +326,34 @@ def tp_linear_row(X, W, Y, P: int, mode: int = TP_ROW_SUM, workspace=None,
     _same_gpu(X, W, Y, workspace)
     check(_get_lib().tp_linear_row(xp, ldx, wp, ldw, yp, ldy, y_slice_stride, mode, wsp, wsb,
                             M, N, K, P, dt, _stream(X, stream)))
+
+
+def tp_linear_row_noalloc(X, W, Y, P: int, mode: int = TP_ROW_SUM, y_slice_stride: int = 0,
+                          stream=None) -> None:
+    """tp_linear_row without a workspace argument: the library's fixed
+    per-GPU array of TP_NOALLOC_SCRATCH_BYTES serves as the workspace, so
+    nothing is allocated (calls that may overlap on one GPU race on it).
+    Shapes whose workspace would exceed it raise TPError(TP_ERR_WORKSPACE)."""
+    xp, M, K, ldx = _mat(X, "X")
+    wp, N, Kw, ldw = _mat(W, "W")
+    if Kw != K:
+        raise ValueError(f"X has K={K} but W has K={Kw}")
+    dt = _dtype_code(X)
+    if _dtype_code(W) != dt:
+        raise TypeError("X and W must share one dtype")
+    _check_p(P)
+    if mode == TP_ROW_PARTIAL:
+        import torch
+        if Y.dtype != torch.float32:
+            raise ValueError("Y must be float32 [P, M, N] for TP_ROW_PARTIAL")
+        yp, ldy = _block_out(Y, P, M, N)
+    else:
+        if _dtype_code(Y) != dt:
+            raise TypeError("Y must have the dtype of X")
+        yp, ldy = _scatter_out(Y, M, N, P, mode == TP_ROW_SCATTER, y_slice_stride)
+    _same_gpu(X, W, Y)
+    check(_get_lib().tp_linear_row_noalloc(xp, ldx, wp, ldw, yp, ldy, y_slice_stride, mode,
+                                           M, N, K, P, dt, _stream(X, stream)))
 
 
 def tp_shard_reduce(partials, Y, P: int, scatter: int = 0, y_slice_stride: int = 0,

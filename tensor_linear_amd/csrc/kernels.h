@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "tplinear.h"
+
 namespace tpl {
 
 // One grouped GEMM over P shards: for i in [0, P)
@@ -114,6 +116,14 @@ struct EmbedArgs {
 hipError_t launch_embedding(const EmbedArgs &e, int elem_bytes, hipStream_t s);
 
 hipError_t launch_fill_zero(void *ptr, size_t words, hipStream_t s);
+
+// Every argument check of tp_linear_row_ex except the workspace's (TP_OK
+// also for empty problems, which queue nothing).  Shared by the entry points
+// so that they reject the same calls with the same status.
+tp_status row_args_status(const void *X, int64_t ldx, const void *W, int64_t ldw,
+                          const void *bias, void *Y, void *const *y_slices, int64_t ldy,
+                          int64_t y_slice_stride, int32_t mode, int64_t M, int64_t N, int64_t K,
+                          int32_t P, int32_t dtype);
 
 // Compute units of the current device (cached per device; 256 if the query
 // fails).  Sizes the persistent grids of the tile kernels.

@@ -222,11 +222,14 @@ size_t tp_row_workspace_bytes(int32_t mode, int64_t M, int64_t N, int32_t P) {
     }
 }
 
-tp_status tp_linear_row_ex(const void *X, int64_t ldx, const void *W, int64_t ldw,
-                           const void *bias, void *Y, void *const *y_slices, int64_t ldy,
-                           int64_t y_slice_stride, int32_t mode, void *workspace,
-                           size_t ws_bytes, int64_t M, int64_t N, int64_t K, int32_t P,
-                           int32_t dtype, void *stream) {
+}  // extern "C"
+
+namespace tpl {
+
+tp_status row_args_status(const void *X, int64_t ldx, const void *W, int64_t ldw,
+                          const void *bias, void *Y, void *const *y_slices, int64_t ldy,
+                          int64_t y_slice_stride, int32_t mode, int64_t M, int64_t N, int64_t K,
+                          int32_t P, int32_t dtype) {
     tp_status st = check_gemm_shape(M, N, K, P, ldx, ldw);
     if (st != TP_OK) return st;
     if (!valid_dtype(dtype)) return TP_ERR_DTYPE;
@@ -250,6 +253,22 @@ tp_status tp_linear_row_ex(const void *X, int64_t ldx, const void *W, int64_t ld
         return TP_ERR_NULL;
     }
     if (K > 0 && (!X || !W)) return TP_ERR_NULL;
+    return TP_OK;
+}
+
+}  // namespace tpl
+
+extern "C" {
+
+tp_status tp_linear_row_ex(const void *X, int64_t ldx, const void *W, int64_t ldw,
+                           const void *bias, void *Y, void *const *y_slices, int64_t ldy,
+                           int64_t y_slice_stride, int32_t mode, void *workspace,
+                           size_t ws_bytes, int64_t M, int64_t N, int64_t K, int32_t P,
+                           int32_t dtype, void *stream) {
+    const tp_status st = row_args_status(X, ldx, W, ldw, bias, Y, y_slices, ldy, y_slice_stride,
+                                         mode, M, N, K, P, dtype);
+    if (st != TP_OK) return st;
+    if (M == 0 || N == 0) return TP_OK;
     const size_t need = tp_row_workspace_bytes(mode, M, N, P);
     if (need > 0 && (!workspace || ws_bytes < need || ((uintptr_t)workspace % WS_ALIGN) != 0))
         return TP_ERR_WORKSPACE;

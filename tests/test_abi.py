@@ -326,3 +326,29 @@ def test_binding_rejects_misshaped_outputs():
     with pytest.raises(tl.TPError) as e:
         tl.tp_shard_reduce(torch.zeros(P, 6, N, dtype=f32), Y(6, N), P, scatter=1)
     assert e.value.status == tl.TP_ERR_INDIVISIBLE
+
+
+def test_noalloc_rejects_before_any_device_call():
+    """tp_linear_row_noalloc: a shape whose workspace would exceed the fixed
+    per-GPU array is TP_ERR_WORKSPACE on the host; argument errors are the
+    ones tp_linear_row reports.  Nothing here reaches a device."""
+    lib = tl.lib
+
+    def call(M, N, K, P, mode=tl.TP_ROW_SUM, ldy=None):
+        return lib.tp_linear_row_noalloc(FX, K, FW, K, FY, N if ldy is None else ldy, 0, mode,
+                                         M, N, K, P, tl.TP_BF16, None)
+    cap = tl.TP_NOALLOC_SCRATCH_BYTES
+    # 4096 x 4096 x 8 fp32 partials = 512 MiB > the array
+    assert tl.tp_row_workspace_bytes(tl.TP_ROW_SUM, 4096, 4096, 8) > cap
+    assert call(4096, 4096, 4096, 8) == tl.TP_ERR_WORKSPACE
+    assert call(4096, 4096, 4096, 8, tl.TP_ROW_SCATTER) == tl.TP_ERR_WORKSPACE
+    # one partial element past the limit
+    M = cap // (4 * 1024 * 8) + 1
+    assert tl.tp_row_workspace_bytes(tl.TP_ROW_SUM, M, 1024, 8) > cap
+    assert call(M, 1024, 64, 8) == tl.TP_ERR_WORKSPACE
+    # argument errors as tp_linear_row
+    assert call(4, 12, 8, 0) == tl.TP_ERR_SHAPE
+    assert call(4, 12, 10, 4) == tl.TP_ERR_INDIVISIBLE
+    assert call(4, 12, 8, 4, mode=9) == tl.TP_ERR_MODE
+    assert call(4, 12, 8, 4, ldy=11) == tl.TP_ERR_SHAPE
+    assert call(0, 12, 8, 4) == tl.TP_OK

@@ -1,0 +1,53 @@
+"""tp_linear_row_noalloc (the row-parallel Linear for callers that cannot
+allocate) against tp_linear_row with a caller workspace: the same kernels, so
+the outputs must be equal bit for bit.  Two calls in a row, the second with a
+smaller input, for every mode that uses the workspace, bf16 and fp32."""
+import numpy as np
+import pytest
+import torch
+
+import tensor_linear_amd as tl
+from gpu_util import DEV, bits, workspace
+
+pytestmark = pytest.mark.gpu
+
+# (M, K, N, P): the first call's partials fill 16 MiB of the 32 MiB array,
+# the second is smaller and ragged
+SHAPES = [(512, 4096, 1024, 8), (72, 600, 200, 4)]
+
+
+def _inputs(M, K, N, dtype, seed):
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(seed)
+    X = torch.randn((M, K), generator=gen, device=DEV).to(dtype)
+    W = (torch.randn((N, K), generator=gen, device=DEV) * 0.02).to(dtype)
+    return X, W
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("mode", [tl.TP_ROW_SUM, tl.TP_ROW_FUSED, tl.TP_ROW_SCATTER,
+                                  tl.TP_ROW_PARTIAL])
+def test_noalloc_equals_workspace_call(dtype, mode):
+    for i, (M, K, N, P) in enumerate(SHAPES):
+        print(f"noalloc mode={mode} dtype={dtype} M={M} K={K} N={N} P={P}", flush=True)
+        assert tl.tp_row_workspace_bytes(mode, M, N, P) <= tl.TP_NOALLOC_SCRATCH_BYTES
+        X, W = _inputs(M, K, N, dtype, 300 + i)
+        if mode == tl.TP_ROW_PARTIAL:
+            ref = torch.empty((P, M, N), dtype=torch.float32, device=DEV)
+            got = torch.full((P, M, N), float("nan"), dtype=torch.float32, device=DEV)
+        else:
+            ref = torch.empty((M, N), dtype=dtype, device=DEV)
+            got = torch.full((M, N), float("nan"), dtype=dtype, device=DEV)
+        tl.tp_linear_row(X, W, ref, P, mode, workspace(mode, M, N, P))
+        tl.tp_linear_row_noalloc(X, W, got, P, mode)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(got), bits(ref)), f"call {i}"
+
+
+def test_noalloc_rejects_oversized_workspace():
+    M, K, N, P = 2048, 64, 1024, 8      # 64 MiB of partials
+    X, W = _inputs(M, K, N, torch.bfloat16, 7)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(tl.TPError) as e:
+        tl.tp_linear_row_noalloc(X, W, Y, P, tl.TP_ROW_SUM)
+    assert e.value.status == tl.TP_ERR_WORKSPACE
