@@ -15,7 +15,8 @@ HIP events on the stream it runs on; `cpu_baseline` times the CPU oracle on a
 bounded sample of the same workload; `context` holds figures taken outside the
 timed step (each GEMM's shards launched alone, in turn, at their real shape, a plain device copy,
 the shader clock while each GEMM runs and the roofline fraction at that clock:
-the chip lowers its clock under sustained matrix-core load).
+the chip lowers its clock under sustained matrix-core load; and the platform's
+own GEMM / gather on the same inputs, timed the same way).
 
 Other workloads (--workload): 3 Llama-70B attention shard, 4 decode, 5
 sequence-parallel round trip, 6 the Llama-8B MLP layer with its column and row
@@ -54,6 +55,8 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=3072,
                     help="rows of X the CPU oracle baseline computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-platform-reference", dest="platform_reference", action="store_false",
+                    help="skip timing the platform's own GEMM / gather on the same inputs")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run 3 device-to-device copies of this many MiB (a plain copy "
                          "of known size, to scale hardware byte counters)")
@@ -427,6 +430,81 @@ def shader_clock(wl, op_stats, steps, step_ms, torch):
     return out
 
 
+def platform_reference(wl, steps, torch):
+    """The platform's own kernels on the same inputs, timed the way the step
+    is (context, not part of the step).  GEMM workloads: the platform GEMM
+    (torch.nn.functional.linear, hipBLASLt) on each column GEMM's dense
+    equivalent -- X [M, K] times all N rows of W, the same flops and the same
+    output -- and on the row GEMM's full-K product (the same flops, one bf16
+    output instead of P fp32 partials).  Embedding: F.embedding of the same
+    batches of ids over the P shard tables concatenated into one [V, D] table
+    (the same bytes moved as the library's lookup), and the per-shard gather
+    followed by torch.cat (what the same lookup costs written with torch ops
+    on the shard tables); both captured with one new batch per launch in a
+    HIP graph and the replay timed, as the embedding step is."""
+    import torch.nn.functional as F
+    out = {}
+
+    def timed(fn, reps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3   # us
+
+    if wl.wid in (2, 3, 5, 6, 7):
+        pairs = []
+        if wl.wid in (2, 3):
+            pairs = [("column_gemm", wl.X1, wl.W1), ("row_gemm_full_k", wl.X2, wl.W2)]
+        elif wl.wid in (5, 7):
+            pairs = [("row_gemm_full_k", wl.X1, wl.W1), ("column_gemm", wl.Y, wl.W3)]
+        elif wl.wid == 6:
+            pairs = [("column_gemm_gate_up", wl.X1, wl.W1), ("row_gemm_full_k", wl.H, wl.W2)]
+        for name, X, W in pairs:
+            fl = 2.0 * X.shape[0] * X.shape[1] * W.shape[0]
+            us = timed(lambda X=X, W=W: F.linear(X, W), max(3, min(20, int(2e13 / fl))))
+            out[name] = dict(avg_us=us, tflops=fl / us / 1e6,
+                             frac_bf16_peak=fl / us / 1e6 / PEAK_BF16_TFLOPS,
+                             kernel="torch.nn.functional.linear (platform GEMM)")
+    elif wl.wid == 8:
+        T, D = wl.ids.shape[0], wl.Y1.shape[1]
+        nbytes = T * D * 2 * 2 + T * 8
+        full = torch.cat(wl.E, dim=1)          # [V, D]: the shard tables side by side
+        for name, fn in (
+                ("embedding_one_table", lambda ids: F.embedding(ids, full)),
+                ("embedding_shard_tables_cat",
+                 lambda ids: torch.cat([F.embedding(ids, e) for e in wl.E], dim=1))):
+            fn(wl.id_sets[0])
+            torch.cuda.synchronize()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                fn(wl.id_sets[0])
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for s in range(steps):
+                    fn(wl.id_sets[s % len(wl.id_sets)])
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / steps * 1e3
+            out[name] = dict(avg_us=us, gbps=nbytes / us / 1e3, frac_hbm_peak=nbytes / us / 1e3 / PEAK_HBM_GBPS)
+            del g
+        del full
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -542,6 +620,7 @@ def main():
     del src, dst
 
     clocks = shader_clock(wl, op_stats, args.steps, ms_step, torch)
+    platform = platform_reference(wl, args.steps, torch) if args.platform_reference else {}
 
     # dominant kernel: the op with the most time
     dom = max(op_stats, key=lambda k: op_stats[k]["avg_us"])
@@ -592,6 +671,8 @@ def main():
                             "on a second stream; bf16 peak assumes "
                             f"{PEAK_CLOCK_GHZ} GHz; none of these is part of the step"},
     }
+    if platform:
+        out["context"]["platform_reference"] = platform
     if graph is not None:
         out["context"]["timing"] = (f"the {args.steps} timed launches captured in one HIP graph "
                                     "(a new batch of ids each) and its replay timed with one "
