@@ -25,23 +25,29 @@
 // c ^ ((r / 2) % 8), so the 16 rows a 16-lane group of ds_read_b128 reads hit
 // 16 different bank groups.  Global -> LDS with global_load_lds_dwordx4 (one
 // 1 KB wave instruction = 8 rows, no register staging).  Each step's 16 loads
-// per wave are spread evenly, 4 per phase: the W half loaded one step ahead
-// has 3-4 phases of lead, the X loaded two steps ahead (the third X stage
-// makes room for it) 5-6 phases -- with two stages of each, a whole step had
-// to be loaded in the two phases after the stage came free.
+// per wave are spread evenly, one every 8th MFMA: the W half loaded one step
+// ahead has 4-6 quarter-steps of lead before the barrier that needs it, the
+// other W half 7-8, the X loaded two steps ahead (the third X stage makes room
+// for it) 9-12 -- with two stages of each, a whole step had to be loaded in
+// the quarter of the step after the stage came free.
 //
-// Per step (K = 64 = two 32-wide substeps), 4 phases of 32 MFMAs (16 cycles
-// each): phases 0-1 substep 0 (W blocks 0-3, then 4-7, each against X blocks
-// 0-7), phases 2-3 substep 1.  One barrier per step, before phase 3; the
-// fragment reads are placed so that each is read well before its first use
-// and no fragment register is overwritten before its last:
-//   phase 0: substep-0 W4-7 of this step, substep-1 X0-3
-//   phase 1: substep-1 W0, X4-7, W1-3
-//   phase 2: substep-1 W4-7
+// Per step (K = 64 = two 32-wide substeps), 8 quarters of 16 MFMAs (16 cycles
+// each), each one 4 x 4 group of the wave's W blocks against its X blocks:
+// q0 W0-3 x X0-3, q1 W0-3 x X4-7, q2 W4-7 x X0-3, q3 W4-7 x X4-7 on substep 0,
+// q4-q7 the same on substep 1.  Every quarter reads four fragments, one every
+// 4th MFMA, so LDS reads flow at one even rate:
+//   q0 X4-7 (substep 0)  q1 W4-7 (0)  q2 W0-3 (1)  q3 X0-3 (1)
+//   q4 X4-7 (1)          q5 W4-7 (1)
 //   (barrier: step it+1 has landed; every wave is done with step it's stages)
-//   phase 3: step it+1 substep-0 W0, X0-7, W1-3
-// DMA loads: phase 0 the second W half of step it+1, phases 1-2 X of step
-// it+2, phase 3 the first W half of step it+2.
+//   q6 W0-3, q7 X0-3 of step it+1's substep 0.
+// A fragment replaces the register of the same block of the other substep,
+// whose last use is at least a quarter earlier.  Inside a quarter the block
+// group read most recently is the slow index, so each of its fragments is
+// first used 16 MFMAs after its read.  One barrier per step, before q6.
+// DMA loads: q0-q1 the second W half of step it+1, q2-q5 X of step it+2,
+// q6-q7 the first W half of step it+2.  (Measured against four 32-MFMA
+// phases with 8, 8, 4 and 12 reads: the same results bit for bit, 0.3-2%
+// faster on every GEMM shape.)
 //
 // Each tile's first MFMA of every accumulator block takes a zero C operand,
 // so no accumulator registers are cleared between tiles.
@@ -246,8 +252,11 @@ void gemm_tile_kernel(GemmArgs g, TileSched ts, int vec_store, GemmExtra ex) {
     auto read_frag = [&](int h, int f, uint32_t addr) __attribute__((always_inline)) {
         fr[h][f] = *(LDS_PTR(bf16x8))(lds + addr);
     };
+    // Step 0's substep-0 W0-3 and X0-3, which its first quarter uses.
 #pragma unroll
-    for (int f = 0; f < 16; ++f) read_frag(0, f, frag_addr(0, W_BASE, f, 0));
+    for (int f = 0; f < 4; ++f) read_frag(0, f, frag_addr(0, W_BASE, f, 0));
+#pragma unroll
+    for (int f = 8; f < 12; ++f) read_frag(0, f, frag_addr(0, W_BASE, f, 0));
 
     int it = 0;
     int xs = 0, ws = 0;       // X stage it % 3, W stage it % 2
@@ -261,14 +270,14 @@ void gemm_tile_kernel(GemmArgs g, TileSched ts, int vec_store, GemmExtra ex) {
             const uint32_t xb = xs * OPB, wb = W_BASE + ws * OPB;
             const uint32_t xb1 = xs1 * OPB, wb1 = W_BASE + ws1 * OPB;
 #pragma unroll
-            for (int ph = 0; ph < 4; ++ph) {
-                if (ph == 3) {
+            for (int qr = 0; qr < 8; ++qr) {
+                if (qr == 6) {
                     __builtin_amdgcn_sched_barrier(0);
-                    // Step it+1's operands have landed (X issued in phases
-                    // 1-2 of step it-1, W in phase 3 of it-1 and phase 0 of
-                    // it); the 8 X loads of step it+2 may stay in flight.
-                    // After an epilogue its stores are in flight too, and a
-                    // store may complete before an older load: wait for all.
+                    // Step it+1's operands have landed (X issued in q2-q5 of
+                    // step it-1, W in q6-q7 of it-1 and q0-q1 of it); the 8 X
+                    // loads of step it+2 may stay in flight.  After an
+                    // epilogue its stores are in flight too, and a store may
+                    // complete before an older load: wait for all.
                     // lgkmcnt(0): this wave's reads of step it's stages are
                     // done before anyone's DMA may overwrite them.
                     if (drained)
@@ -279,50 +288,44 @@ void gemm_tile_kernel(GemmArgs g, TileSched ts, int vec_store, GemmExtra ex) {
                     drained = true;
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                const int h = ph >> 1;
+                const int h = qr >> 2;                       // substep
+                const int wg = (qr >> 1) & 1, xg = qr & 1;   // W blocks 4wg.., X blocks 4xg..
+                const bool x_outer = (qr & 3) != 2;          // X blocks the slow index
 #pragma unroll
-                for (int u = 0; u < 32; ++u) {
+                for (int u = 0; u < 16; ++u) {
                     __builtin_amdgcn_sched_barrier(0);
-                    const int i = (ph & 1) * 4 + (u >> 3), j = u & 7;
+                    const int a = u >> 2, b = u & 3;
+                    const int i = wg * 4 + (x_outer ? b : a), j = xg * 4 + (x_outer ? a : b);
                     if (FIRST && h == 0)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[0][i], fr[0][8 + j], f32x4{}, 0, 0, 0);
                     else
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[h][i], fr[h][8 + j], acc[i][j], 0, 0, 0);
-                    // reads: every 4th slot in phases 0-1 (8), every 8th in
-                    // phase 2 (4), every other in phase 3 (12)
-                    const int rs = ph == 3 ? 2 : (ph == 2 ? 8 : 4);
-                    const int nrd = ph == 3 ? 12 : (ph == 2 ? 4 : 8);
-                    const bool rd = (u % rs) == 0 && u / rs < nrd;
+                    const bool rd = (u & 3) == 0;
                     if (rd) {
-                        const int k = u / rs;
-                        if (ph == 0) {
-                            if (k < 4) read_frag(0, 4 + k, frag_addr(xb, wb, 4 + k, 0));
-                            else read_frag(1, 8 + (k - 4), frag_addr(xb, wb, 8 + (k - 4), 1));
-                        } else if (ph == 1) {
-                            const int f = k == 0 ? 0 : (k <= 4 ? 8 + 4 + (k - 1) : k - 4);
-                            read_frag(1, f, frag_addr(xb, wb, f, 1));
-                        } else if (ph == 2) {
-                            read_frag(1, 4 + k, frag_addr(xb, wb, 4 + k, 1));
-                        } else {
-                            const int f = k == 0 ? 0 : (k <= 8 ? 8 + (k - 1) : k - 8);
-                            read_frag(0, f, frag_addr(xb1, wb1, f, 0));
+                        const int k = u >> 2;
+                        switch (qr) {
+                            case 0: read_frag(0, 12 + k, frag_addr(xb, wb, 12 + k, 0)); break;  // X4-7 sub 0
+                            case 1: read_frag(0, 4 + k, frag_addr(xb, wb, 4 + k, 0)); break;    // W4-7 sub 0
+                            case 2: read_frag(1, k, frag_addr(xb, wb, k, 1)); break;            // W0-3 sub 1
+                            case 3: read_frag(1, 8 + k, frag_addr(xb, wb, 8 + k, 1)); break;    // X0-3 sub 1
+                            case 4: read_frag(1, 12 + k, frag_addr(xb, wb, 12 + k, 1)); break;  // X4-7 sub 1
+                            case 5: read_frag(1, 4 + k, frag_addr(xb, wb, 4 + k, 1)); break;    // W4-7 sub 1
+                            case 6: read_frag(0, k, frag_addr(xb1, wb1, k, 0)); break;          // next W0-3
+                            default: read_frag(0, 8 + k, frag_addr(xb1, wb1, 8 + k, 0)); break; // next X0-3
                         }
                     }
-                    // DMA loads every 8th slot, between the reads
-                    const int l0 = ph == 3 ? 1 : (ph == 2 ? 4 : 2);
-                    const bool ld = u >= l0 && (u - l0) % 8 == 0;
+                    const bool ld = (u & 7) == 2;
                     if (ld) {
-                        const int l = (u - l0) / 8;   // 0..3
-                        if (ph == 0) load_w(ws1, 4 + l);        // second W half of step it+1
-                        else if (ph == 1) load_x(xs2, l);       // X of step it+2
-                        else if (ph == 2) load_x(xs2, 4 + l);
-                        else load_w(ws, l);                     // first W half of step it+2
+                        const int l = (qr & 1) * 2 + (u >> 3);   // 0..3 within a pair of quarters
+                        if (qr < 2) load_w(ws1, 4 + l);                     // second W half of step it+1
+                        else if (qr < 6) load_x(xs2, ((qr - 2) >> 1) * 4 + l);  // X of step it+2
+                        else load_w(ws, l);                                 // first W half of step it+2
                     }
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
                     if (rd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                if (ph == 0) advance();
+                if (qr == 1) advance();
             }
             __builtin_amdgcn_sched_barrier(0);
             xs = xs1;
