@@ -387,12 +387,20 @@ void gemm_tile_kernel(GemmArgs g, TileSched ts, int vec_store, GemmExtra ex) {
                                 for (int e = 0; e < 8; ++e) bv[e] = n + e < g.N ? (float)bias[n + e] : 0.0f;
                             }
                         }
+                        // All of the group's LDS reads first, so that they
+                        // overlap each other rather than each waiting on
+                        // its own store.
+                        f32x4 a0[4], a1[4];
 #pragma unroll
                         for (int p = 0; p < 4; ++p) {
                             const int rr = p * 8 + (lane >> 3);
-                            const f32x4 a0 = *(LDS_PTR(f32x4))st_addr(rr, 2 * c8);
-                            const f32x4 a1 = *(LDS_PTR(f32x4))st_addr(rr, 2 * c8 + 1);
-                            float v[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+                            a0[p] = *(LDS_PTR(f32x4))st_addr(rr, 2 * c8);
+                            a1[p] = *(LDS_PTR(f32x4))st_addr(rr, 2 * c8 + 1);
+                        }
+#pragma unroll
+                        for (int p = 0; p < 4; ++p) {
+                            float v[8] = {a0[p][0], a0[p][1], a0[p][2], a0[p][3],
+                                          a1[p][0], a1[p][1], a1[p][2], a1[p][3]};
                             if (has_bias) {
 #pragma unroll
                                 for (int e = 0; e < 8; ++e) v[e] = v[e] + bv[e];
@@ -419,25 +427,31 @@ void gemm_tile_kernel(GemmArgs g, TileSched ts, int vec_store, GemmExtra ex) {
                             }
                         }
                     } else {
-                        // lane: row p*4 + lane/16, 4 columns from 4*(lane%16)
+                        // lane: row p*4 + lane/16, 4 columns from 4*(lane%16);
+                        // the reads first, as above
+                        const int sl = lane & 15;
+                        f32x4 a[8];
 #pragma unroll
-                        for (int p = 0; p < 8; ++p) {
-                            const int rr = p * 4 + (lane >> 4), sl = lane & 15;
-                            const f32x4 a = *(LDS_PTR(f32x4))st_addr(rr, sl);
-                            const int64_t mrow = tm_w + j * 32 + p * 4;
-                            if (interior) {
+                        for (int p = 0; p < 8; ++p) a[p] = *(LDS_PTR(f32x4))st_addr(p * 4 + (lane >> 4), sl);
+                        if (interior) {
+#pragma unroll
+                            for (int p = 0; p < 8; ++p) {
+                                const int64_t mrow = tm_w + j * 32 + p * 4;
                                 char *rb = (char *)g.C + (cbase + mrow * g.ldc + ncol) * 4;
-                                __builtin_nontemporal_store(a, (f32x4 *)(rb + lane_off));
-                            } else {
-                                const int64_t m = mrow + (lane >> 4), n = ncol + sl * 4;
+                                __builtin_nontemporal_store(a[p], (f32x4 *)(rb + lane_off));
+                            }
+                        } else {
+#pragma unroll
+                            for (int p = 0; p < 8; ++p) {
+                                const int64_t m = tm_w + j * 32 + p * 4 + (lane >> 4), n = ncol + sl * 4;
                                 if (m < g.M) {
                                     float *dst = (float *)g.C + cbase + m * g.ldc + n;
                                     if (vec_store && n + 4 <= g.N) {
-                                        __builtin_nontemporal_store(a, (f32x4 *)dst);
+                                        __builtin_nontemporal_store(a[p], (f32x4 *)dst);
                                     } else {
 #pragma unroll
                                         for (int e = 0; e < 4; ++e)
-                                            if (n + e < g.N) dst[e] = a[e];
+                                            if (n + e < g.N) dst[e] = a[p][e];
                                     }
                                 }
                             }

@@ -327,10 +327,10 @@ tp_status tp_linear_row_ex(const void *X, int64_t ldx, const void *W, int64_t ld
     // narrower tile moves 1.5x the operand bytes per flop, so it wins only
     // while the shard's K is short -- the shorter, the smaller the output.
     // Fused / unfused time measured on one box with cold caches (a 1 GiB
-    // write before each call), P = 8: M = N = 4096: K/P = 1024 0.88, 1280
-    // 0.95, 1536 1.03, 1792 1.08, 2048 1.08; M = N = 8192: 1024 0.77, 1280
-    // 0.87, 1536 0.94, 1792 0.95, 2048 1.03.
-    const bool fold_in_gemm = Ks <= 1280 || (Ks <= 1792 && M * N >= (int64_t)8192 * 8192);
+    // write before each call), P = 8: M = N = 4096: K/P = 1024 0.91, 1280
+    // 1.03, 1536 1.11, 1792 1.18, 2048 1.19; M = N = 8192: 1024 0.80, 1280
+    // 0.94, 1536 1.02, 1792 1.03, 2048 1.14.
+    const bool fold_in_gemm = Ks <= 1024 || (Ks <= 1280 && M * N >= (int64_t)8192 * 8192);
     if ((mode == TP_ROW_FUSED || mode == TP_ROW_SCATTER) && dtype == TP_BF16 && fold_in_gemm &&
         gemm_rowfold_supported(g, r))
         return hip_status(launch_gemm_rowfold(g, r, s));
