@@ -299,15 +299,17 @@ hipError_t launch_gemm_skinny(const GemmArgs &g, int out_type, const FoldArgs *f
     // keeps more loads in flight when the grid is large (one workgroup per
     // 16 output columns and shard: three 16 KB stages, two in flight).  The
     // fused fold has a P times smaller grid: one workgroup per CU with 32
-    // output columns and five 24 KB stages, four in flight.  Measured with
+    // output columns and four 24 KB stages, three in flight.  Measured with
     // M = 16, K = 8192, N = 28672 over 8 shards: column 82-83 us with 3 or 4
     // stages of 256 columns against 88-89 with 2; fused fold of 8 shards of
     // K = 3584, N = 8192: 82-83 us with 32 columns and 3-6 stages, 86-87 with
     // 16 columns and two 512-column stages; a later same-box sweep gave 86.6
     // us for this choice against 85.9 (32 columns, 3 stages), 89.6-90.8 (16
     // columns: 3 or 4 stages of 256, 2 of 512), 97.6 (32 columns, 2 stages of
-    // 512) and 147.7 (64 columns: half the CUs idle).  The gated unit streams 32 W rows
-    // (16 gate, 16 up) per workgroup with the column form's stages.
+    // 512) and 147.7 (64 columns: half the CUs idle); three later same-box
+    // runs of 2-6 stages of 256 put 4 stages 2-7% ahead of 5 (6 stages 5% and
+    // 2 stages 25% behind).  The gated unit streams 32 W rows (16 gate, 16
+    // up) per workgroup with the column form's stages.
     if (ex.act == ACT_SWIGLU) {
         if (fold) return hipErrorInvalidValue;
         if (g.M <= 16) return launch_mb<2, 1, 256, 3, true>(g, out_type, fold, ex, s);   // 72 KB
@@ -315,7 +317,7 @@ hipError_t launch_gemm_skinny(const GemmArgs &g, int out_type, const FoldArgs *f
         return launch_mb<2, 4, 256, 2, true>(g, out_type, fold, ex, s);                  // 96 KB
     }
     if (g.M <= 16) {
-        if (fold) return launch_mb<2, 1, 256, 5>(g, out_type, fold, ex, s);   // 120 KB
+        if (fold) return launch_mb<2, 1, 256, 4>(g, out_type, fold, ex, s);   // 96 KB
         return launch_mb<1, 1, 256, 3>(g, out_type, fold, ex, s);             // 48 KB
     }
     if (g.M <= 32) return launch_mb<1, 2, 256, 2>(g, out_type, fold, ex, s);  // 48 KB
