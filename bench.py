@@ -122,9 +122,10 @@ class Workload:
             self.H = torch.empty((M, I), dtype=bf, device=dev)
             self.Y2 = torch.empty((M, H), dtype=bf, device=dev)
             self.parts = torch.empty((P, M, H), dtype=torch.float32, device=dev)
-            # The row layer as the library runs TP_ROW_FUSED at this shape
-            # (shard K 1792, 4096 x 4096 output): fp32 partials, then the fold
-            # with the bias -- here faster than the fold in registers.
+            # The row layer as its two explicit stages: fp32 partials, then
+            # the fold with the Partial bias (TP_ROW_FUSED would fold inside
+            # the GEMM at this shape; the step keeps the fold kernel with the
+            # bias measured).
             self.ops = [
                 ("column_gemm_swiglu_bias", 2.0 * M * 2 * I * H, None,
                  lambda: tl.tp_linear_column_ex(self.X1, self.W1, self.H, P, bias=self.b1,
@@ -242,7 +243,8 @@ class Workload:
             row("row_gemm_one_shard", self.X2, self.W2, False)
             # the whole row layer (all P shards) through TP_ROW_FUSED, launched
             # back to back: the library folds inside the GEMM where that is
-            # faster (the Llama-70B O layer), else runs partials + fold
+            # faster (both layers here: shard K 1792 and 1024), else runs
+            # partials + fold
             M, N = self.X2.shape[0], self.W2.shape[0]
             Yf = torch.empty((M, N), dtype=bf, device=dev)
             wsf = torch.empty(tl.tp_row_workspace_bytes(tl.TP_ROW_FUSED, M, N, P),
@@ -663,8 +665,8 @@ def main():
                     "note": "one_shard: each GEMM's shards launched alone at their real shape "
                             "(one GPU's share), one after another (so a shard is not still "
                             "cached from the launch before), and for the prefill workloads the whole row layer "
-                            "through TP_ROW_FUSED back to back (the fold inside the GEMM for the "
-                            "Llama-70B O layer, partials + fold for fc2); device_copy_gbps: read+write bytes of a 1 GiB "
+                            "through TP_ROW_FUSED back to back (the fold inside the GEMM, bitwise equal to "
+                            "partials + fold); device_copy_gbps: read+write bytes of a 1 GiB "
                             "device-to-device copy per second; shader_clock_ghz: the shader "
                             "clock idle, while each GEMM of the step runs back to back (2.5 ms "
                             "window) and over a replay of the timed steps, from a probe kernel "

@@ -167,7 +167,7 @@ tp_status tp_linear_column(const void *X, int64_t ldx, const void *W, int64_t ld
  *   a running fp32 sum, so no partial reaches memory and the workspace is
  *   not touched.  That holds for bf16 operands (16-byte aligned, leading
  *   dims and shard offsets multiples of 8) with 1 <= M <= 64, or with K/P a
- *   multiple of 64 and at most 1024 (at most 1280 when M*N >= 8192*8192),
+ *   multiple of 64 and at most 2048 (at most 3584 when M*N >= 4096*4096),
  *   where the in-register fold measured faster.  Other shapes run the
  *   TP_ROW_SUM sequence in the workspace, which is therefore always
  *   required.

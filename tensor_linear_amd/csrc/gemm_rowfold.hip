@@ -5,24 +5,30 @@
 //
 // A workgroup owns one 256 (tokens) x 128 (output features) tile and walks
 // the P shards in ascending order.  Shard i's partial X_i W_i^T is computed
-// in 128 accumulator registers (2 x 4 v_mfma_f32_32x32x16_bf16 blocks per
-// wave, the same instruction and the same K order as the partial GEMM), then
-// added into a running fp32 sum held in another 128 registers:
+// in 128 accumulator registers per lane (4 waves in a 2x2 grid, each a
+// 128 x 64 block of 8 x 4 v_mfma_f32_16x16x32_bf16 blocks, the instruction
+// and K order of the partial GEMM), then added into a running fp32 sum held
+// in another 128 registers:
 //   run = p_0;  run = run + p_i  (i = 1 .. P-1);  Y = rne(run [+ bias]).
 // These are the operations, in the order, of writing the P fp32 partials and
 // folding them, so the result is bitwise equal to that unfused sequence; no
 // partial reaches memory and no workspace is needed.  The tile is half as
-// wide as the partial GEMM's (the running sum takes the other half of the
-// register budget), so each K step moves 1.5x the operand bytes per flop;
-// the gain is the 2 P M N x 4 bytes of partials that are neither written nor
-// read back.
+// wide as the partial GEMM's (the running sum takes the registers the other
+// half of the accumulators would), so each K step moves 1.5x the operand
+// bytes per flop; the gain is the 2 P M N x 4 bytes of partials that are
+// neither written nor read back.
 //
-// Pipeline, as in the partial GEMM: global -> LDS with global_load_lds_dwordx4
-// (16 bytes per lane), two stages of 64 K columns (48 KB each), 128-byte LDS
-// rows with 16-byte chunk c of row r at slot c ^ ((r / 2) % 8); per K step
-// four phases of 8 MFMAs with the next sub-step's 6 fragment reads and the
-// global loads interleaved, the W part of the next step issued in phase 0,
-// the X part of the step after it in phase 3 behind the step's one barrier.
+// Pipeline: global -> LDS with global_load_lds_dwordx4 (1 KB per wave
+// instruction), three stages of 64 K columns for both operands (3 x (32 +
+// 16) KB = 144 KB), 128-byte LDS rows with 16-byte chunk c of row r at slot
+// c ^ ((r / 2) % 8).  Step it+2's 12 loads per wave go out in the first
+// three quarters of step it, one every 4th MFMA, into the stage step it-1
+// freed.  Per K step 4 quarters of 16 MFMAs (a 4 x 4 group of W x X blocks):
+//   q0 W0-3 x X0-3, q1 W0-3 x X4-7 on substep 0, q2, q3 the same on
+//   substep 1;
+// fragment reads: q0 X4-7 (substep 0) and W0-1 (1), q1 W2-3 and X0-3 (1),
+// q2 X4-7 (1); then the step's one barrier; q3 the next step's substep-0
+// W0-3 and X0-3, interleaved so that q0 can start on the first pair.
 // Persistent: one workgroup per CU walks an XCD-contiguous range of tiles,
 // and the K pipeline runs across shard and tile boundaries.
 #include "kernels.h"
@@ -32,7 +38,6 @@ namespace tpl {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_PTR(T) __attribute__((address_space(3))) T *
@@ -71,26 +76,29 @@ __device__ __forceinline__ int fold_tile_of(const FoldSched &ts, int q) {
     return t < ts.T ? t : -1;
 }
 
+// q0's MFMA order: the next step's fragments arrive X0, W0, X1, W1, ...;
+// (W block, X block) pairs in the order they become ready.
+__device__ __forceinline__ constexpr int q0_w(int u) {
+    return u < 4 ? (u >> 1) : (u < 9 ? (u < 6 ? u - 4 : 2) : (u < 12 ? u - 9 : 3));
+}
+__device__ __forceinline__ constexpr int q0_x(int u) {
+    return u < 4 ? (u & 1) : (u < 9 ? (u < 6 ? 2 : u - 6) : (u < 12 ? 3 : u - 12));
+}
+
 // ro: where the folded tile goes (Y, ldy, the token slices of a
 // reduce-scatter, the bias); its partials fields are unused.
 template <bool SCAT>
 __global__ __attribute__((amdgpu_flat_work_group_size(FT, FT), amdgpu_waves_per_eu(1, 1)))
 void gemm_rowfold_kernel(GemmArgs g, FoldSched ts, ReduceArgs ro, int vec_store) {
     constexpr int ROWB = FBK * 2;          // 128 bytes per LDS row
-    constexpr int CPR = FBK / 8;           // 16-byte chunks per row
-    constexpr int RP = 256 / ROWB;         // rows per 256 bytes
-    constexpr int OPX = FM * ROWB;         // X tile, 32 KB
-    constexpr int OPW = FN * ROWB;         // W tile, 16 KB
-    constexpr int STAGE = OPX + OPW;
-    constexpr int RPI = 1024 / ROWB;       // rows per 1 KB load instruction
-    constexpr int LX = OPX / 1024 / 4;     // X loads per wave per step
-    constexpr int LW = OPW / 1024 / 4;     // W loads per wave per step
-    constexpr int KS = FBK / 16;           // MFMA k-steps per stage
-    constexpr int EPI_ROWB = 32 * 4 + 16;
-    constexpr int EPI_WAVE = 32 * EPI_ROWB;
-    static_assert(2 * STAGE + 4 * EPI_WAVE <= 160 * 1024, "LDS");
-    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE + 4 * EPI_WAVE];
+    constexpr int OPX = FM * ROWB;         // X stage, 32 KB
+    constexpr int OPW = FN * ROWB;         // W stage, 16 KB
+    constexpr int W_BASE = 3 * OPX;        // three X stages, then three W stages
+    constexpr int LX = OPX / 1024 / 4;     // X loads per wave per step (8)
+    constexpr int LW = OPW / 1024 / 4;     // W loads per wave per step (4)
+    __shared__ __attribute__((aligned(1024))) char smem[3 * OPX + 3 * OPW];
     LDS_PTR(char) lds = (LDS_PTR(char))smem;
+    const uint32_t lds_u = (uint32_t)(uintptr_t)lds;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -104,8 +112,9 @@ void gemm_rowfold_kernel(GemmArgs g, FoldSched ts, ReduceArgs ro, int vec_store)
     const int P = g.P;
     const int total = ntiles * P * nk;
 
-    // ---- prefetch cursor: (tile pq, shard psh, step pkt), NST-1 = 1 step
-    // ahead of the compute cursor; past the last step it stays there.
+    // ---- load cursor: (tile pq, shard psh, step pkt), two steps ahead of
+    // the compute; past the last step it stays there, so later issues reload
+    // the last step into stages that are not read again.
     int pq = 0, psh = 0, pkt = 0, pstep = 0;
     int64_t pm0 = 0, pn0 = 0;
     const char *pa = nullptr, *pb = nullptr;
@@ -119,15 +128,15 @@ void gemm_rowfold_kernel(GemmArgs g, FoldSched ts, ReduceArgs ro, int vec_store)
         const int b_rows = (int)min<int64_t>(g.N - pn0, FN);
 #pragma unroll
         for (int j = 0; j < LX; ++j) {
-            const int r = (j * 4 + wave) * RPI + lane / CPR;
-            const int chunk = (lane % CPR) ^ ((r / RP) % CPR);
+            const int r = (j * 4 + wave) * 8 + lane / 8;
+            const int chunk = (lane % 8) ^ ((r / 2) % 8);
             const int ra = r < a_rows ? r : a_rows - 1;
             aoff[j] = (uint32_t)(((int64_t)ra * g.lda + chunk * 8) * 2);
         }
 #pragma unroll
         for (int j = 0; j < LW; ++j) {
-            const int r = (j * 4 + wave) * RPI + lane / CPR;
-            const int chunk = (lane % CPR) ^ ((r / RP) % CPR);
+            const int r = (j * 4 + wave) * 8 + lane / 8;
+            const int chunk = (lane % 8) ^ ((r / 2) % 8);
             const int rb = r < b_rows ? r : b_rows - 1;
             boff[j] = (uint32_t)(((int64_t)rb * g.ldb + chunk * 8) * 2);
         }
@@ -135,23 +144,6 @@ void gemm_rowfold_kernel(GemmArgs g, FoldSched ts, ReduceArgs ro, int vec_store)
     auto set_bases = [&]() {
         pa = (const char *)((const __bf16 *)g.A + (int64_t)psh * g.a_shard + pm0 * g.lda);
         pb = (const char *)((const __bf16 *)g.B + (int64_t)psh * g.b_shard + pn0 * g.ldb);
-    };
-    // Loads [j0, j1) of the cursor's step into `stage`: 0..LX-1 fill the X
-    // tile, LX..LX+LW-1 the W tile.
-    auto issue_part = [&](int stage, int j0, int j1) {
-        LDS_PTR(char) dst = lds + stage * STAGE;
-        const int64_t kb = (int64_t)pkt * FBK * 2;
-#pragma unroll
-        for (int j = 0; j < LX + LW; ++j) {
-            if (j < j0 || j >= j1) continue;
-            if (j < LX)
-                __builtin_amdgcn_global_load_lds((const void *)(pa + kb + aoff[j]),
-                                                 (LDS_PTR(void))(dst + (j * 4 + wave) * 1024), 16, 0, 0);
-            else
-                __builtin_amdgcn_global_load_lds(
-                    (const void *)(pb + kb + boff[j - LX]),
-                    (LDS_PTR(void))(dst + OPX + ((j - LX) * 4 + wave) * 1024), 16, 0, 0);
-        }
     };
     auto advance = [&]() {
         if (pstep + 1 < total) {
@@ -167,171 +159,223 @@ void gemm_rowfold_kernel(GemmArgs g, FoldSched ts, ReduceArgs ro, int vec_store)
             }
         }
     };
+    // One 1 KB DMA load, issued as an instruction the compiler does not
+    // track (its own wait analysis cannot tell which stage a DMA writes);
+    // the waits the pipeline needs are written out below.
+    auto dma = [&](const char *base, uint32_t voff, uint32_t lds_addr) __attribute__((always_inline)) {
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                     :: "v"(voff), "s"(base), "s"(lds_addr) : "memory", "m0");
+    };
+    // Load l (0..11) of the cursor's step into stage `slot`: 0..7 the X
+    // tile, 8..11 the W tile.
+    auto load = [&](int slot, int l) __attribute__((always_inline)) {
+        if (l < LX)
+            dma(pa + (int64_t)pkt * 128, aoff[l], lds_u + slot * OPX + (l * 4 + wave) * 1024);
+        else
+            dma(pb + (int64_t)pkt * 128, boff[l - LX],
+                lds_u + W_BASE + slot * OPW + ((l - LX) * 4 + wave) * 1024);
+    };
 
+    // Prologue: steps 0 and 1 into stages 0 and 1.
     enter_tile(0);
     set_bases();
-    issue_part(0, 0, LX + LW);
+#pragma unroll
+    for (int l = 0; l < LX + LW; ++l) load(0, l);
     advance();
-    issue_part(1, 0, LX);
-
-    // Fragment addressing (32x32x16 operands: lane reads row lane%32,
-    // k-chunk 2*ks + lane/32).
-    const int frow = lane & 31;
-    const int fhalf = lane >> 5;
-    const int fx = (frow / RP) % CPR;
-    const int wrow_off = (wn * 64 + frow) * ROWB;
-    const int xrow_off = (wm * 128 + frow) * ROWB;
-
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    bf16x8 wf[2][2], xf[2][4];
-    {
-        const int slot = ((0 + fhalf) ^ fx) << 4;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) wf[0][i] = *(LDS_PTR(bf16x8))(lds + OPX + wrow_off + i * 32 * ROWB + slot);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) xf[0][j] = *(LDS_PTR(bf16x8))(lds + xrow_off + j * 32 * ROWB + slot);
-    }
+    for (int l = 0; l < LX + LW; ++l) load(1, l);
+    advance();
+    asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    asm volatile("s_barrier" ::: "memory");
 
-    int it = 0;
-    f32x16 acc[2][4], run[2][4];
+    // Fragments (16 rows x 32 k): lane reads row lane%16 of its block,
+    // 16-byte k-chunk 4*h + lane/16 of substep h.  fr[h][0..3] W blocks
+    // (output features 16i.. of the wave's 64), fr[h][4..11] X blocks
+    // (tokens 16j.. of the wave's 128).
+    const int frow = lane & 15;
+    const int fq = lane >> 4;
+    const int fx = (frow / 2) % 8;
+    const uint32_t wrow_off = (wn * 64 + frow) * ROWB;
+    const uint32_t xrow_off = (wm * 128 + frow) * ROWB;
+    auto frag_addr = [&](int stage, int f, int h) -> uint32_t {
+        const uint32_t slot = (uint32_t)(((4 * h + fq) ^ fx) << 4);
+        if (f < 4) return W_BASE + stage * OPW + wrow_off + f * 16 * ROWB + slot;
+        return stage * OPX + xrow_off + (f - 4) * 16 * ROWB + slot;
+    };
+    bf16x8 fr[2][12];
+    auto read_frag = [&](int h, int f, uint32_t addr) __attribute__((always_inline)) {
+        fr[h][f] = *(LDS_PTR(bf16x8))(lds + addr);
+    };
+#pragma unroll
+    for (int f = 0; f < 8; ++f) read_frag(0, f, frag_addr(0, f, 0));
+
+    int s0 = 0;                 // stage of the current step (step index % 3)
+    bool drained = true;        // no epilogue store is in flight
+    f32x4 acc[4][8], run[4][8];
     for (int q = 0; q < ntiles; ++q) {
         for (int sh = 0; sh < P; ++sh) {
-            // One K step: KS phases of 8 MFMAs; the next sub-step's 6
-            // fragment reads in slots 0-5; the W loads of the step after
-            // this one in phase 0 (slots 4-7), the X loads of the step two
-            // ahead in the last phase (one per slot), behind the barrier
-            // that frees their stage.
             auto kstep = [&](auto first) __attribute__((always_inline)) {
                 constexpr bool FIRST = decltype(first)::value;
-                LDS_PTR(char) st = lds + (it & 1) * STAGE;
-                LDS_PTR(char) st_next = lds + ((it + 1) & 1) * STAGE;
+                const int s1 = s0 == 2 ? 0 : s0 + 1;   // stage of step it+1
+                const int s2 = s1 == 2 ? 0 : s1 + 1;   // stage of step it+2 (= it-1's)
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const int cur = ks & 1, nx = cur ^ 1;
-                    if (ks == KS - 1) {
+                for (int qr = 0; qr < 4; ++qr) {
+                    if (qr == 3) {
                         __builtin_amdgcn_sched_barrier(0);
-                        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                        __syncthreads();
-                    }
-                    LDS_PTR(char) rd = ks + 1 < KS ? st : st_next;
-                    const int rks = ks + 1 < KS ? ks + 1 : 0;
-                    const int slot = ((2 * rks + fhalf) ^ fx) << 4;
-                    int j0 = LX + LW, j1 = LX + LW, s0 = 0;
-                    if (ks == 0) { j0 = LX; j1 = LX + LW; s0 = 4; }     // W of step it+1
-                    if (ks == KS - 1) { j0 = 0; j1 = LX; s0 = 0; }      // X of step it+2
-                    const int lstage = ks == 0 ? (it + 1) & 1 : it & 1;
-#pragma unroll
-                    for (int u = 0; u < 8; ++u) {
-                        __builtin_amdgcn_sched_barrier(0);
-                        // Order (i, j): the first four MFMAs touch all six
-                        // fragments.
-                        const int i = u & 1, j = (u + (u >> 2)) & 3;
-                        if (FIRST && ks == 0)   // the shard's first product of each block: C = 0
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][i], xf[cur][j],
-                                                                                f32x16{}, 0, 0, 0);
+                        // Step it+1's loads (issued in step it-1) have
+                        // landed; step it+2's 12 may stay in flight.  This
+                        // wave's reads of step it's stage are done before
+                        // anyone's loads may overwrite it (two steps on).
+                        // After an epilogue its stores are in flight too,
+                        // and a store may complete before an older load:
+                        // then wait for all.
+                        if (drained)
+                            asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)" ::: "memory");
                         else
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][i], xf[cur][j],
-                                                                                acc[i][j], 0, 0, 0);
-                        if (u < 6) {
-                            if (u < 2)
-                                wf[nx][u] = *(LDS_PTR(bf16x8))(rd + OPX + wrow_off + u * 32 * ROWB + slot);
-                            else
-                                xf[nx][u - 2] = *(LDS_PTR(bf16x8))(rd + xrow_off + (u - 2) * 32 * ROWB + slot);
-                        }
-                        const int la = j0 + (u - s0);
-                        const bool ld = u >= s0 && la < j1;
-                        if (ld) issue_part(lstage, la, la + 1);
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // MFMA
-                        if (u < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-                        if (ld) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // VMEM
-                    }
-                    if (ks == 0) {
+                            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+                        drained = true;
+                        asm volatile("s_barrier" ::: "memory");
                         __builtin_amdgcn_sched_barrier(0);
-                        advance();
                     }
+                    const int h = qr >> 1;
+#pragma unroll
+                    for (int u = 0; u < 16; ++u) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        int i, j;
+                        if (qr == 0) {
+                            i = q0_w(u);
+                            j = q0_x(u);
+                        } else {
+                            i = u & 3;
+                            j = (qr & 1) * 4 + (u >> 2);
+                        }
+                        if (FIRST && h == 0)   // the shard's first product of each block: C = 0
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[0][i], fr[0][4 + j], f32x4{}, 0, 0, 0);
+                        else
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[h][i], fr[h][4 + j], acc[i][j], 0, 0, 0);
+                        // fragment reads
+                        bool rd = false;
+                        if (qr == 0 && (u & 1) == 0 && u < 12) {
+                            const int k = u >> 1;   // 0..5
+                            if (k < 4) read_frag(0, 8 + k, frag_addr(s0, 8 + k, 0));   // X4-7 substep 0
+                            else read_frag(1, k - 4, frag_addr(s0, k - 4, 1));         // W0-1 substep 1
+                            rd = true;
+                        } else if (qr == 1 && (u & 1) == 0 && u < 12) {
+                            const int k = u >> 1;
+                            if (k < 2) read_frag(1, 2 + k, frag_addr(s0, 2 + k, 1));   // W2-3 substep 1
+                            else read_frag(1, 4 + (k - 2), frag_addr(s0, 4 + (k - 2), 1));   // X0-3
+                            rd = true;
+                        } else if (qr == 2 && (u & 3) == 0) {
+                            const int k = u >> 2;
+                            read_frag(1, 8 + k, frag_addr(s0, 8 + k, 1));             // X4-7 substep 1
+                            rd = true;
+                        } else if (qr == 3 && (u & 1) == 0) {
+                            const int k = u >> 1;   // X0, W0, X1, W1, ... of step it+1
+                            const int f = (k & 1) ? (k >> 1) : 4 + (k >> 1);
+                            read_frag(0, f, frag_addr(s1, f, 0));
+                            rd = true;
+                        }
+                        // step it+2's loads, one every 4th MFMA in q0-q2
+                        const bool ld = qr < 3 && (u & 3) == 1;
+                        if (ld) load(s2, qr * 4 + (u >> 2));
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                        if (rd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (qr == 2) advance();
                 }
                 __builtin_amdgcn_sched_barrier(0);
+                s0 = s1;
             };
             kstep(std::true_type{});
-            ++it;
-            for (int kt = 1; kt < nk; ++kt, ++it) kstep(std::false_type{});
+            for (int kt = 1; kt < nk; ++kt) kstep(std::false_type{});
             // The fold: one fp32 add per shard, ascending.
             if (sh == 0) {
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) run[i][j] = acc[i][j];
+                    for (int j = 0; j < 8; ++j) run[i][j] = acc[i][j];
             } else {
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) run[i][j] = run[i][j] + acc[i][j];
+                    for (int j = 0; j < 8; ++j) run[i][j] = run[i][j] + acc[i][j];
             }
         }
 
-        // ---- epilogue: run (+ bias) -> bf16.  Each 32x32 block goes
-        // through this wave's LDS area, written in its MFMA layout (lane:
-        // token lane%32, four consecutive features per register group) and
-        // read back row-contiguous: lane holds 8 consecutive features of one
-        // token row, 16-byte stores.
+        // ---- epilogue: run (+ bias) -> bf16.  run[i][j][r] = Y[m = 16j +
+        // lane%16][n = 16i + 4*(lane/16) + r] of the wave's block.  32 rows x
+        // 64 columns at a time go through this wave's 1 KB chunks w + 4c
+        // (c = 0..7) of the X stage of the tile's last step (read by everyone
+        // before that step's barrier; only this wave's own later loads write
+        // these chunks): staging row r of 256 bytes at chunk r/4, offset
+        // (r%4)*256, 16-byte slot s at s ^ (r % 16).  Each lane then holds 8
+        // consecutive features of one row: a row of 64 features leaves as one
+        // 128-byte line.
+        __builtin_amdgcn_sched_barrier(0);
         int tm, tn;
         fold_decode(ts, fold_tile_of(ts, q), tm, tn);
-        const int64_t tm_w = (int64_t)tm * FM + wm * 128, tn_w = (int64_t)tn * FN + wn * 64;
-        LDS_PTR(char) ep = lds + 2 * STAGE + wave * EPI_WAVE;
-        const int lr = lane >> 2, lc = 8 * (lane & 3);
+        const int es = s0 == 0 ? 2 : s0 - 1;
+        LDS_PTR(char) ep = lds + es * OPX + wave * 1024;
+        auto st_addr = [&](int r, int s) -> LDS_PTR(char) {
+            return ep + (r >> 2) * 4096 + (r & 3) * 256 + ((s ^ (r & 15)) << 4);
+        };
+        const int64_t m_t = (int64_t)tm * FM, tm_w = m_t + wm * 128, tn_w = (int64_t)tn * FN + wn * 64;
+        __bf16 *ybase;   // row m_t of the output (tile rows never span two slices)
+        if (SCAT) {
+            const int64_t sl = m_t / ro.slice_rows, rr = m_t - sl * ro.slice_rows;
+            ybase = ro.use_slices ? (__bf16 *)ro.y_slice[sl] + rr * ro.ldy
+                                  : (__bf16 *)ro.Y + sl * ro.slice_stride + rr * ro.ldy;
+        } else {
+            ybase = (__bf16 *)ro.Y + m_t * ro.ldy;
+        }
         const __bf16 *bias = (const __bf16 *)ro.bias;
+        const int c8 = lane & 7;
+        const int64_t ncol = tn_w + c8 * 8;
+        float bv[8];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            float bv[8];
+        for (int e = 0; e < 8; ++e) bv[e] = bias && ncol + e < g.N ? (float)bias[ncol + e] : 0.0f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int64_t n = tn_w + i * 32 + lc + e;
-                bv[e] = bias && n < g.N ? (float)bias[n] : 0.0f;
+        for (int jj = 0; jj < 4; ++jj) {        // rows 32jj.. of the wave
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+                for (int bi = 0; bi < 4; ++bi)
+                    *(LDS_PTR(f32x4))st_addr(bj * 16 + frow, bi * 4 + fq) = run[bi][2 * jj + bj];
+            f32x4 a0[4], a1[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int rr = p * 8 + (lane >> 3);
+                a0[p] = *(LDS_PTR(f32x4))st_addr(rr, 2 * c8);
+                a1[p] = *(LDS_PTR(f32x4))st_addr(rr, 2 * c8 + 1);
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                __builtin_amdgcn_sched_barrier(0);
+            for (int p = 0; p < 4; ++p) {
+                const int rr = p * 8 + (lane >> 3);
+                const int64_t m = tm_w + jj * 32 + rr;
+                if (m >= g.M) continue;
+                float v[8] = {a0[p][0], a0[p][1], a0[p][2], a0[p][3], a1[p][0], a1[p][1], a1[p][2], a1[p][3]};
+                bf16x8 hv;
 #pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const f32x4 v = {run[i][j][4 * r4], run[i][j][4 * r4 + 1],
-                                     run[i][j][4 * r4 + 2], run[i][j][4 * r4 + 3]};
-                    *(LDS_PTR(f32x4))(ep + frow * EPI_ROWB + (8 * r4 + 4 * fhalf) * 4) = v;
-                }
+                for (int e = 0; e < 8; ++e) hv[e] = (__bf16)(bias ? v[e] + bv[e] : v[e]);
+                __bf16 *row = ybase + (m - m_t) * ro.ldy;
+                if (vec_store && ncol + 8 <= g.N) {
+                    __builtin_nontemporal_store(hv, (bf16x8 *)(row + ncol));
+                } else {
 #pragma unroll
-                for (int pp = 0; pp < 2; ++pp) {
-                    LDS_PTR(char) rp = ep + (pp * 16 + lr) * EPI_ROWB + lc * 4;
-                    const f32x4 a0 = *(LDS_PTR(f32x4))rp, a1 = *(LDS_PTR(f32x4))(rp + 16);
-                    float v[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-                    const int64_t m = tm_w + j * 32 + pp * 16 + lr, n = tn_w + i * 32 + lc;
-                    if (m >= g.M) continue;
-                    bf16x8 hv;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) hv[e] = (__bf16)(bias ? v[e] + bv[e] : v[e]);
-                    __bf16 *row;
-                    if (SCAT) {
-                        const int64_t sl = m / ro.slice_rows, rr = m - sl * ro.slice_rows;
-                        row = ro.use_slices ? (__bf16 *)ro.y_slice[sl] + rr * ro.ldy
-                                            : (__bf16 *)ro.Y + sl * ro.slice_stride + rr * ro.ldy;
-                    } else {
-                        row = (__bf16 *)ro.Y + m * ro.ldy;
-                    }
-                    if (vec_store && n + 8 <= g.N) {
-                        __builtin_nontemporal_store(hv, (bf16x8 *)(row + n));
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            if (n + e < g.N) row[n + e] = hv[e];
-                    }
+                    for (int e = 0; e < 8; ++e)
+                        if (ncol + e < g.N) row[ncol + e] = hv[e];
                 }
             }
         }
+        drained = false;
     }
+    // No DMA load may still be writing LDS when the workgroup ends.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
-
 
 }  // namespace
 

@@ -325,12 +325,13 @@ tp_status tp_linear_row_ex(const void *X, int64_t ldx, const void *W, int64_t ld
     // Prefill shapes: the fold in registers (256x128 tiles walking the P
     // shards) saves writing and re-reading the P fp32 partials, but its
     // narrower tile moves 1.5x the operand bytes per flop, so it wins only
-    // while the shard's K is short -- the shorter, the smaller the output.
-    // Fused / unfused time measured on one box with cold caches (a 1 GiB
-    // write before each call), P = 8: M = N = 4096: K/P = 1024 0.91, 1280
-    // 1.03, 1536 1.11, 1792 1.18, 2048 1.19; M = N = 8192: 1024 0.80, 1280
-    // 0.94, 1536 1.02, 1792 1.03, 2048 1.14.
-    const bool fold_in_gemm = Ks <= 1024 || (Ks <= 1280 && M * N >= (int64_t)8192 * 8192);
+    // while the shard's K is short enough -- the shorter, the smaller the
+    // output.  Fused / unfused time measured on one box with cold caches (a
+    // 1 GiB write before each call), P = 8: M x N = 2048 x 4096: K/P = 1024
+    // 0.73, 2048 0.93; 4096 x 4096: 1024 0.74, 1792 0.86, 2560 0.93, 3584
+    // 0.97, 5120 1.03; 8192 x 8192: 1024 0.64, 1280 0.71, 1792 0.75, 3584
+    // 0.93, 7168 1.04; 16384 x 8192: 3584 0.92, 7168 1.02.
+    const bool fold_in_gemm = Ks <= 2048 || (Ks <= 3584 && M * N >= (int64_t)4096 * 4096);
     if ((mode == TP_ROW_FUSED || mode == TP_ROW_SCATTER) && dtype == TP_BF16 && fold_in_gemm &&
         gemm_rowfold_supported(g, r))
         return hip_status(launch_gemm_rowfold(g, r, s));

@@ -16,8 +16,8 @@ pytestmark = pytest.mark.gpu
 
 SHAPES = [
     # (M, K, N, P, bias)
-    (512, 8192, 4096, 8, False),    # K/P = 1024, the longest shard K taken at any size
-    (8192, 10240, 8192, 8, False),  # K/P = 1280 with an 8192 x 8192 output
+    (512, 16384, 4096, 8, False),   # K/P = 2048, the longest shard K taken at any size
+    (4096, 28672, 4096, 8, False),  # K/P = 3584 with a 4096 x 4096 output
     (264, 8192, 8192, 8, True),     # Llama-70B O, K/P = 1024, ragged M tile
     (300, 1024, 1000, 8, True),     # ragged N tile (1000 = 7 x 128 + 104)
     (256, 256, 136, 2, False),
