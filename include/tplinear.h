@@ -335,10 +335,13 @@ tp_status tp_embedding(const int64_t *ids, int64_t T, const void *E,
  * GPU, kept until the process ends).  The call allocates nothing and calls no
  * allocating routine; the array's device address on the current device is
  * looked up once per device, on its first call there.
- * Limit: tp_row_workspace_bytes(mode, M, N, P) <= TP_NOALLOC_SCRATCH_BYTES,
- *   else TP_ERR_WORKSPACE before anything is queued (modes and shapes that
- *   need no workspace -- TP_ROW_PARTIAL, and the fused paths -- are not
- *   limited).  No part of the array has to start at zero: every partial is
+ * Limit: the calls that fold fp32 partials in a separate kernel --
+ *   TP_ROW_SUM, and TP_ROW_FUSED / TP_ROW_SCATTER at the shapes where the
+ *   fold does not run inside the GEMM (see TP_ROW_FUSED) -- need
+ *   tp_row_workspace_bytes(mode, M, N, P) <= TP_NOALLOC_SCRATCH_BYTES, else
+ *   TP_ERR_WORKSPACE before anything is queued; TP_ROW_PARTIAL and the
+ *   calls whose fold runs inside the GEMM use no workspace and have no such
+ *   limit.  No part of the array has to start at zero: every partial is
  *   written before the fold reads it.
  * Concurrency: all calls on one GPU share that GPU's array and it keeps the
  *   last call's contents, so calls that may overlap on one GPU (on different

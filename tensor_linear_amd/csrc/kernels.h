@@ -125,6 +125,24 @@ tp_status row_args_status(const void *X, int64_t ldx, const void *W, int64_t ldw
                           int64_t y_slice_stride, int32_t mode, int64_t M, int64_t N, int64_t K,
                           int32_t P, int32_t dtype);
 
+// The launch plan of a row-parallel call that passed row_args_status and is
+// not empty: the kernels tp_linear_row_ex runs for it (which depend on the
+// mode, dtype and shape), built without touching any memory.  Only
+// PARTIALS_AND_FOLD uses the workspace (P fp32 [M, N] partials, row stride
+// N); the other paths write the output directly.
+struct RowPlan {
+    enum Path { PARTIAL, SKINNY_FOLD, ROWFOLD, PARTIALS_AND_FOLD } path;
+    GemmArgs g; ReduceArgs r; FoldArgs f; GemmExtra ex;
+    int out; int32_t dtype;
+};
+tp_status plan_row(const void *X, int64_t ldx, const void *W, int64_t ldw, const void *bias,
+                   void *Y, void *const *y_slices, int64_t ldy, int64_t y_slice_stride,
+                   int32_t mode, int64_t M, int64_t N, int64_t K, int32_t P, int32_t dtype,
+                   RowPlan &plan);
+// Queue the plan's kernels; `workspace` is read only by PARTIALS_AND_FOLD
+// (TP_ERR_WORKSPACE if it is null there).
+tp_status run_row(RowPlan &plan, float *workspace, hipStream_t s);
+
 // Compute units of the current device (cached per device; 256 if the query
 // fails).  Sizes the persistent grids of the tile kernels.
 int device_cu_count();

@@ -58,14 +58,17 @@ extern "C" tp_status tp_linear_row_noalloc(const void *X, int64_t ldx, const voi
                                                y_slice_stride, mode, M, N, K, P, dtype);
     if (chk != TP_OK) return chk;
     if (M == 0 || N == 0) return TP_OK;
-    // The workspace this call needs (0 for modes that need none).
-    const size_t need = tp_row_workspace_bytes(mode, M, N, P);
-    if (need > (size_t)TP_NOALLOC_SCRATCH_BYTES) return TP_ERR_WORKSPACE;
+    tpl::RowPlan plan;
+    const tp_status pst = tpl::plan_row(X, ldx, W, ldw, nullptr, Y, nullptr, ldy, y_slice_stride,
+                                        mode, M, N, K, P, dtype, plan);
+    if (pst != TP_OK) return pst;
+    // Only the partials-and-fold path uses a workspace: the P fp32 partials.
     void *ws = nullptr;
-    if (need > 0) {
+    if (plan.path == tpl::RowPlan::PARTIALS_AND_FOLD) {
+        if (tp_row_workspace_bytes(mode, M, N, P) > (size_t)TP_NOALLOC_SCRATCH_BYTES)
+            return TP_ERR_WORKSPACE;
         const tp_status st = current_scratch(&ws);
         if (st != TP_OK) return st;
     }
-    return tp_linear_row(X, ldx, W, ldw, Y, ldy, y_slice_stride, mode, ws,
-                         need > 0 ? (size_t)TP_NOALLOC_SCRATCH_BYTES : 0, M, N, K, P, dtype, stream);
+    return tpl::run_row(plan, (float *)ws, (hipStream_t)stream);
 }

@@ -256,24 +256,12 @@ tp_status row_args_status(const void *X, int64_t ldx, const void *W, int64_t ldw
     return TP_OK;
 }
 
-}  // namespace tpl
-
-extern "C" {
-
-tp_status tp_linear_row_ex(const void *X, int64_t ldx, const void *W, int64_t ldw,
-                           const void *bias, void *Y, void *const *y_slices, int64_t ldy,
-                           int64_t y_slice_stride, int32_t mode, void *workspace,
-                           size_t ws_bytes, int64_t M, int64_t N, int64_t K, int32_t P,
-                           int32_t dtype, void *stream) {
-    const tp_status st = row_args_status(X, ldx, W, ldw, bias, Y, y_slices, ldy, y_slice_stride,
-                                         mode, M, N, K, P, dtype);
-    if (st != TP_OK) return st;
-    if (M == 0 || N == 0) return TP_OK;
-    const size_t need = tp_row_workspace_bytes(mode, M, N, P);
-    if (need > 0 && (!workspace || ws_bytes < need || ((uintptr_t)workspace % WS_ALIGN) != 0))
-        return TP_ERR_WORKSPACE;
-
-    const hipStream_t s = (hipStream_t)stream;
+// The kernels tp_linear_row_ex runs for a call that passed
+// row_args_status (non-empty), and whether they use the workspace.
+tp_status plan_row(const void *X, int64_t ldx, const void *W, int64_t ldw, const void *bias,
+                   void *Y, void *const *y_slices, int64_t ldy, int64_t y_slice_stride,
+                   int32_t mode, int64_t M, int64_t N, int64_t K, int32_t P, int32_t dtype,
+                   RowPlan &p) {
     const int64_t Ks = K / P;
     // Shard strides from the placements: X [M, K] and W [N, K] Shard(1)
     // (column blocks); the partials Partial() (P [M, N] buffers back to
@@ -282,34 +270,35 @@ tp_status tp_linear_row_ex(const void *X, int64_t ldx, const void *W, int64_t ld
     const int64_t x_stride = view_stride(M, K, ldx, TP_SHARD, 1, P);
     const int64_t w_stride = view_stride(N, K, ldw, TP_SHARD, 1, P);
     if (x_stride < 0 || w_stride < 0) return TP_ERR_SHAPE;
-    GemmArgs g;
+    GemmArgs &g = p.g;
     g.A = X; g.lda = ldx; g.a_shard = x_stride;
     g.B = W; g.ldb = ldw; g.b_shard = w_stride;
     g.M = M; g.N = N; g.K = Ks; g.P = P;
-    const int out = dtype == TP_BF16 ? OUT_BF16 : OUT_F32;
+    p.dtype = dtype;
+    p.out = dtype == TP_BF16 ? OUT_BF16 : OUT_F32;
+    p.ex = GemmExtra{};
+    p.ex.bias = bias;
 
     if (mode == TP_ROW_PARTIAL) {
         const int64_t p_stride = view_stride(M, N, ldy, TP_PARTIAL, 0, P);
         if (p_stride < 0) return TP_ERR_SHAPE;
         g.C = Y; g.ldc = ldy; g.c_shard = p_stride;
-        return hip_status(run_gemm(g, dtype, OUT_F32, nullptr, s));
+        p.path = RowPlan::PARTIAL;
+        return TP_OK;
     }
 
     const int64_t p_stride = view_stride(M, N, N, TP_PARTIAL, 0, P);
     if (p_stride < 0) return TP_ERR_SHAPE;
-    float *parts = (float *)workspace;
-    g.C = parts; g.ldc = N; g.c_shard = p_stride;
+    g.C = nullptr; g.ldc = N; g.c_shard = p_stride;   // the workspace, set by run_row
 
     if (mode == TP_ROW_FUSED && dtype == TP_BF16 && gemm_skinny_supported(g, nullptr)) {
-        FoldArgs f;
-        f.Y = Y; f.ldy = ldy; f.out_type = out;
-        GemmExtra ex{};
-        ex.bias = bias;
-        return hip_status(launch_gemm_skinny(g, out, &f, bias ? &ex : nullptr, s));
+        p.f.Y = Y; p.f.ldy = ldy; p.f.out_type = p.out;
+        p.path = RowPlan::SKINNY_FOLD;
+        return TP_OK;
     }
 
-    ReduceArgs r;
-    r.partials = parts; r.shard_stride = p_stride; r.ldp = N;
+    ReduceArgs &r = p.r;
+    r.partials = nullptr; r.shard_stride = p_stride; r.ldp = N;
     r.Y = Y; r.ldy = ldy; r.M = M; r.N = N; r.P = P;
     r.bias = bias;
     set_out_slices(r, y_slices, P);
@@ -333,12 +322,55 @@ tp_status tp_linear_row_ex(const void *X, int64_t ldx, const void *W, int64_t ld
     // 0.93, 7168 1.04; 16384 x 8192: 3584 0.92, 7168 1.02.
     const bool fold_in_gemm = Ks <= 2048 || (Ks <= 3584 && M * N >= (int64_t)4096 * 4096);
     if ((mode == TP_ROW_FUSED || mode == TP_ROW_SCATTER) && dtype == TP_BF16 && fold_in_gemm &&
-        gemm_rowfold_supported(g, r))
-        return hip_status(launch_gemm_rowfold(g, r, s));
+        gemm_rowfold_supported(g, r)) {
+        p.path = RowPlan::ROWFOLD;
+        return TP_OK;
+    }
+    p.path = RowPlan::PARTIALS_AND_FOLD;
+    return TP_OK;
+}
 
-    hipError_t e = run_gemm(g, dtype, OUT_F32, nullptr, s);
-    if (e != hipSuccess) return TP_ERR_HIP;
-    return hip_status(launch_shard_fold(r, out, s));
+tp_status run_row(RowPlan &p, float *workspace, hipStream_t s) {
+    switch (p.path) {
+        case RowPlan::PARTIAL:
+            return hip_status(run_gemm(p.g, p.dtype, OUT_F32, nullptr, s));
+        case RowPlan::SKINNY_FOLD:
+            return hip_status(launch_gemm_skinny(p.g, p.out, &p.f, p.ex.bias ? &p.ex : nullptr, s));
+        case RowPlan::ROWFOLD:
+            return hip_status(launch_gemm_rowfold(p.g, p.r, s));
+        case RowPlan::PARTIALS_AND_FOLD:
+        default: {
+            if (!workspace) return TP_ERR_WORKSPACE;
+            p.g.C = workspace;
+            p.r.partials = workspace;
+            const hipError_t e = run_gemm(p.g, p.dtype, OUT_F32, nullptr, s);
+            if (e != hipSuccess) return TP_ERR_HIP;
+            return hip_status(launch_shard_fold(p.r, p.out, s));
+        }
+    }
+}
+
+}  // namespace tpl
+
+extern "C" {
+
+tp_status tp_linear_row_ex(const void *X, int64_t ldx, const void *W, int64_t ldw,
+                           const void *bias, void *Y, void *const *y_slices, int64_t ldy,
+                           int64_t y_slice_stride, int32_t mode, void *workspace,
+                           size_t ws_bytes, int64_t M, int64_t N, int64_t K, int32_t P,
+                           int32_t dtype, void *stream) {
+    const tp_status st = row_args_status(X, ldx, W, ldw, bias, Y, y_slices, ldy, y_slice_stride,
+                                         mode, M, N, K, P, dtype);
+    if (st != TP_OK) return st;
+    if (M == 0 || N == 0) return TP_OK;
+    const size_t need = tp_row_workspace_bytes(mode, M, N, P);
+    if (need > 0 && (!workspace || ws_bytes < need || ((uintptr_t)workspace % WS_ALIGN) != 0))
+        return TP_ERR_WORKSPACE;
+    RowPlan plan;
+    const tp_status pst = plan_row(X, ldx, W, ldw, bias, Y, y_slices, ldy, y_slice_stride, mode,
+                                   M, N, K, P, dtype, plan);
+    if (pst != TP_OK) return pst;
+    return run_row(plan, (float *)workspace, (hipStream_t)stream);
 }
 
 tp_status tp_linear_row(const void *X, int64_t ldx, const void *W, int64_t ldw, void *Y,

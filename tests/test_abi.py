@@ -338,10 +338,13 @@ def test_noalloc_rejects_before_any_device_call():
         return lib.tp_linear_row_noalloc(FX, K, FW, K, FY, N if ldy is None else ldy, 0, mode,
                                          M, N, K, P, tl.TP_BF16, None)
     cap = tl.TP_NOALLOC_SCRATCH_BYTES
-    # 4096 x 4096 x 8 fp32 partials = 512 MiB > the array
+    # 4096 x 4096 x 8 fp32 partials = 512 MiB > the array; TP_ROW_SUM always
+    # folds them in a separate kernel, TP_ROW_FUSED and TP_ROW_SCATTER do at
+    # a shard K of 8192 (too long for the fold inside the GEMM)
     assert tl.tp_row_workspace_bytes(tl.TP_ROW_SUM, 4096, 4096, 8) > cap
     assert call(4096, 4096, 4096, 8) == tl.TP_ERR_WORKSPACE
-    assert call(4096, 4096, 4096, 8, tl.TP_ROW_SCATTER) == tl.TP_ERR_WORKSPACE
+    assert call(4096, 4096, 8 * 8192, 8, tl.TP_ROW_SCATTER) == tl.TP_ERR_WORKSPACE
+    assert call(4096, 4096, 8 * 8192, 8, tl.TP_ROW_FUSED) == tl.TP_ERR_WORKSPACE
     # one partial element past the limit
     M = cap // (4 * 1024 * 8) + 1
     assert tl.tp_row_workspace_bytes(tl.TP_ROW_SUM, M, 1024, 8) > cap

@@ -1,7 +1,9 @@
 """tp_linear_row_noalloc (the row-parallel Linear for callers that cannot
 allocate) against tp_linear_row with a caller workspace: the same kernels, so
 the outputs must be equal bit for bit.  Two calls in a row, the second with a
-smaller input, for every mode that uses the workspace, bf16 and fp32."""
+smaller input, for every mode that uses the workspace, bf16 and fp32; calls
+whose fold runs inside the GEMM at sizes whose partials would not fit the
+fixed array; and the rejection of a call whose partials would not."""
 import numpy as np
 import pytest
 import torch
@@ -42,6 +44,25 @@ def test_noalloc_equals_workspace_call(dtype, mode):
         tl.tp_linear_row_noalloc(X, W, got, P, mode)
         torch.cuda.synchronize()
         assert np.array_equal(bits(got), bits(ref)), f"call {i}"
+
+
+@pytest.mark.parametrize("M,K,N,P,mode", [
+    (2048, 8192, 1024, 8, tl.TP_ROW_FUSED),     # prefill, the fold in registers
+    (2048, 8192, 1024, 8, tl.TP_ROW_SCATTER),   # the same, into 256-row token slices
+    (64, 512, 32768, 8, tl.TP_ROW_FUSED),       # decode, the fused skinny fold
+])
+def test_noalloc_fused_paths_need_no_workspace(M, K, N, P, mode):
+    # 64 MiB of fp32 partials would not fit the array, but these calls fold
+    # inside the GEMM and use none of it
+    print(f"noalloc fused M={M} K={K} N={N} P={P} mode={mode}", flush=True)
+    assert tl.tp_row_workspace_bytes(mode, M, N, P) > tl.TP_NOALLOC_SCRATCH_BYTES
+    X, W = _inputs(M, K, N, torch.bfloat16, 11)
+    ref = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    got = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    tl.tp_linear_row(X, W, ref, P, mode, workspace(mode, M, N, P))
+    tl.tp_linear_row_noalloc(X, W, got, P, mode)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(got), bits(ref))
 
 
 def test_noalloc_rejects_oversized_workspace():
