@@ -66,7 +66,7 @@ def _free(wl):
 @pytest.mark.parametrize("wid", [2, 3])
 def test_prefill_workload_sampled_rows(wid):
     """Column GEMM, row GEMM partials and the shard fold (Llama-8B MLP shard,
-    Llama-70B attention shard)."""
+    Llama-70B attention shard); the fused row layer against that fold."""
     print(f"workload {wid}", flush=True)
     wl = bench.Workload(wid, torch, tl, synth)
     _run(wl)
@@ -85,6 +85,18 @@ def test_prefill_workload_sampled_rows(wid):
     for i in range(P):
         _check(f"row partial {i}", got_parts[i], parts[i], sh["K2"] // P)
     _check("row fold Y2", _host64(wl.Y2[rows]), oracle.fold_f64(parts), sh["K2"])
+
+    # the whole row layer through TP_ROW_FUSED (the fold in registers at
+    # these shard K): bit for bit the fold of the partials above, all rows
+    M, N = wl.Y2.shape
+    Yf = torch.full((M, N), float("nan"), dtype=wl.Y2.dtype, device=wl.Y2.device)
+    ws = torch.empty(tl.tp_row_workspace_bytes(tl.TP_ROW_FUSED, M, N, P), dtype=torch.uint8,
+                     device=wl.Y2.device)
+    print("  launch row layer TP_ROW_FUSED", flush=True)
+    tl.tp_linear_row(wl.X2, wl.W2, Yf, P, tl.TP_ROW_FUSED, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(Yf.view(torch.int16), wl.Y2.view(torch.int16))
+    del Yf, ws
     _free(wl)
 
 
@@ -122,6 +134,17 @@ def test_sequence_parallel_workload_sampled_rows():
     slices = wl.Y.view(P, s, N)
     got = np.stack([_host64(slices[m // s, m % s]) for m in rows])
     _check("reduce-scatter slices", got, oracle.fold_f64(parts), K)
+
+    # TP_ROW_SCATTER in one call (the fold in registers at this shard K):
+    # bit for bit the slices above, all rows
+    Ys = torch.full_like(wl.Y, float("nan"))
+    ws = torch.empty(tl.tp_row_workspace_bytes(tl.TP_ROW_SCATTER, M, N, P), dtype=torch.uint8,
+                     device=wl.Y.device)
+    print("  launch row layer TP_ROW_SCATTER", flush=True)
+    tl.tp_linear_row(wl.X1, wl.W1, Ys, P, tl.TP_ROW_SCATTER, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(Ys.view(torch.int16), wl.Y.view(torch.int16))
+    del Ys, ws
 
     # The next column GEMM reads the gathered slices.  The oracle's input
     # is its own bf16 result of the row stage (fp32 partials, fp32 fold,
