@@ -489,19 +489,23 @@ void gemm_tile_kernel(GemmArgs g, TileSched ts, int vec_store, GemmExtra ex) {
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) *(LDS_PTR(f32x4))sw_addr(frow, i * 4 + fq) = acc[i][j];
+                // both row groups' LDS reads first, then the unit and the stores
+                f32x4 gq[2][2], uq[2][2];
 #pragma unroll
                 for (int p = 0; p < 2; ++p) {
                     const int rr = p * 8 + (lane >> 3);
-                    const f32x4 g0 = *(LDS_PTR(f32x4))sw_addr(rr, 2 * c8);
-                    const f32x4 g1 = *(LDS_PTR(f32x4))sw_addr(rr, 2 * c8 + 1);
-                    const f32x4 u0 = *(LDS_PTR(f32x4))sw_addr(rr, 16 + 2 * c8);
-                    const f32x4 u1 = *(LDS_PTR(f32x4))sw_addr(rr, 16 + 2 * c8 + 1);
-                    const float gv[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
-                    const float uv[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+                    gq[p][0] = *(LDS_PTR(f32x4))sw_addr(rr, 2 * c8);
+                    gq[p][1] = *(LDS_PTR(f32x4))sw_addr(rr, 2 * c8 + 1);
+                    uq[p][0] = *(LDS_PTR(f32x4))sw_addr(rr, 16 + 2 * c8);
+                    uq[p][1] = *(LDS_PTR(f32x4))sw_addr(rr, 16 + 2 * c8 + 1);
+                }
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    const int rr = p * 8 + (lane >> 3);
                     bf16x8 hv;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        float gg = gv[e], uu = uv[e];
+                        float gg = gq[p][e >> 2][e & 3], uu = uq[p][e >> 2][e & 3];
                         if (has_bias) {
                             gg = gg + bg[e];
                             uu = uu + bu[e];
