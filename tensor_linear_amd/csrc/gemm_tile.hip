@@ -34,10 +34,11 @@
 // Per step (K = 64 = two 32-wide substeps), 8 quarters of 16 MFMAs (16 cycles
 // each), each one 4 x 4 group of the wave's W blocks against its X blocks:
 // q0 W0-3 x X0-3, q1 W0-3 x X4-7, q2 W4-7 x X0-3, q3 W4-7 x X4-7 on substep 0,
-// q4-q7 the same on substep 1.  Every quarter reads four fragments, one every
-// 4th MFMA, so LDS reads flow at one even rate:
+// q4-q7 the same on substep 1.  The quarters read four fragments each, one
+// every 4th MFMA, except q4 (eight) and q5 (none), so that no read is still in
+// flight when the wave reaches the barrier:
 //   q0 X4-7 (substep 0)  q1 W4-7 (0)  q2 W0-3 (1)  q3 X0-3 (1)
-//   q4 X4-7 (1)          q5 W4-7 (1)
+//   q4 X4-7 and W4-7 (1) q5 -
 //   (barrier: step it+1 has landed; every wave is done with step it's stages)
 //   q6 W0-3, q7 X0-3 of step it+1's substep 0.
 // A fragment replaces the register of the same block of the other substep,
@@ -47,7 +48,7 @@
 // DMA loads: q0-q1 the second W half of step it+1, q2-q5 X of step it+2,
 // q6-q7 the first W half of step it+2.  (Measured against four 32-MFMA
 // phases with 8, 8, 4 and 12 reads: the same results bit for bit, 0.3-2%
-// faster on every GEMM shape.)
+// faster on every GEMM shape; moving q5's reads into q4 another ~0.5%.)
 //
 // Each tile's first MFMA of every accumulator block takes a zero C operand,
 // so no accumulator registers are cleared between tiles.
@@ -300,7 +301,11 @@ void gemm_tile_kernel(GemmArgs g, TileSched ts, int vec_store, GemmExtra ex) {
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[0][i], fr[0][8 + j], f32x4{}, 0, 0, 0);
                     else
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[h][i], fr[h][8 + j], acc[i][j], 0, 0, 0);
-                    const bool rd = (u & 3) == 0;
+                    // q4 also reads W4-7 of substep 1 (slots 1, 5, 9, 13) and q5
+                    // reads nothing, so that no read is in flight at the barrier
+                    const bool rd2 = qr == 4 && (u & 3) == 1;
+                    if (rd2) read_frag(1, 4 + (u >> 2), frag_addr(xb, wb, 4 + (u >> 2), 1));
+                    const bool rd = (u & 3) == 0 && qr != 5;
                     if (rd) {
                         const int k = u >> 2;
                         switch (qr) {
@@ -309,7 +314,6 @@ void gemm_tile_kernel(GemmArgs g, TileSched ts, int vec_store, GemmExtra ex) {
                             case 2: read_frag(1, k, frag_addr(xb, wb, k, 1)); break;            // W0-3 sub 1
                             case 3: read_frag(1, 8 + k, frag_addr(xb, wb, 8 + k, 1)); break;    // X0-3 sub 1
                             case 4: read_frag(1, 12 + k, frag_addr(xb, wb, 12 + k, 1)); break;  // X4-7 sub 1
-                            case 5: read_frag(1, 4 + k, frag_addr(xb, wb, 4 + k, 1)); break;    // W4-7 sub 1
                             case 6: read_frag(0, k, frag_addr(xb1, wb1, k, 0)); break;          // next W0-3
                             default: read_frag(0, 8 + k, frag_addr(xb1, wb1, 8 + k, 0)); break; // next X0-3
                         }
@@ -322,7 +326,7 @@ void gemm_tile_kernel(GemmArgs g, TileSched ts, int vec_store, GemmExtra ex) {
                         else load_w(ws, l);                                 // first W half of step it+2
                     }
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                    if (rd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+                    if (rd || rd2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 if (qr == 1) advance();
