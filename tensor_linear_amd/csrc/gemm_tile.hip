@@ -41,8 +41,8 @@
 //   q4 X4-7 and W4-7 (1) q5 -
 //   (barrier: step it+1 has landed; every wave is done with step it's stages)
 //   q6 W0-3, q7 X0-3 of step it+1's substep 0.
-// A fragment replaces the register of the same block of the other substep,
-// whose last use is at least a quarter earlier.  Inside a quarter the block
+// A fragment replaces the same block's fragment of the step before, whose
+// last use is at least a quarter earlier.  Inside a quarter the block
 // group read most recently is the slow index, so each of its fragments is
 // first used 16 MFMAs after its read.  One barrier per step, before q6.
 // DMA loads: q0-q1 the second W half of step it+1, q2-q5 X of step it+2,
@@ -56,8 +56,8 @@
 // Epilogue: 32 output rows x 64 columns at a time go through this wave's part
 // of the X stage the tile's last barrier freed (its own 1 KB DMA chunks, which
 // only its own later loads overwrite): written in the MFMA layout, read back
-// row-contiguous, so a bf16 row leaves as one full 128-byte line and an fp32
-// row as two.  Stores are non-temporal (measured faster than cached stores
+// row-contiguous (a group's reads all issued before its stores), so a bf16
+// row leaves as one full 128-byte line and an fp32 row as two.  Stores are non-temporal (measured faster than cached stores
 // for every shape: the burst of all CUs' tiles would fill the L2 with dirty
 // lines the next loads wait behind).
 //
