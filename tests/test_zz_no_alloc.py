@@ -3,7 +3,8 @@ allocate) against tp_linear_row with a caller workspace: the same kernels, so
 the outputs must be equal bit for bit.  Two calls in a row, the second with a
 smaller input, for every mode that uses the workspace, bf16 and fp32; calls
 whose fold runs inside the GEMM at sizes whose partials would not fit the
-fixed array; and the rejection of a call whose partials would not."""
+fixed array; captured in a HIP graph and replayed; and the rejection of a
+call whose partials would not fit."""
 import numpy as np
 import pytest
 import torch
@@ -63,6 +64,41 @@ def test_noalloc_fused_paths_need_no_workspace(M, K, N, P, mode):
     tl.tp_linear_row_noalloc(X, W, got, P, mode)
     torch.cuda.synchronize()
     assert np.array_equal(bits(got), bits(ref))
+
+
+@pytest.mark.parametrize("M,K,N,P,mode", [
+    (512, 4096, 1024, 8, tl.TP_ROW_SUM),        # partials in the fixed array, then the fold
+    (2048, 8192, 1024, 8, tl.TP_ROW_FUSED),     # the fold in registers, no array
+])
+def test_noalloc_under_graph_capture(M, K, N, P, mode):
+    # the callers the entry point is for: a captured step, replayed with new
+    # inputs written eagerly between replays, each replay bitwise equal to
+    # the workspace call run eagerly (the first call, which looks up the
+    # array's address, runs before the capture, on a side stream)
+    print(f"noalloc graph M={M} K={K} N={N} P={P} mode={mode}", flush=True)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(21)
+    X = torch.randn((M, K), generator=gen, device=DEV).to(torch.bfloat16)
+    W = (torch.randn((N, K), generator=gen, device=DEV) * 0.02).to(torch.bfloat16)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        tl.tp_linear_row_noalloc(X, W, Y, P, mode)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        tl.tp_linear_row_noalloc(X, W, Y, P, mode)
+    torch.cuda.synchronize()
+    ws = workspace(mode, M, N, P)
+    for r in range(3):
+        X.copy_(torch.randn((M, K), generator=gen, device=DEV).to(torch.bfloat16))
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = torch.empty_like(Y)
+        tl.tp_linear_row(X, W, ref, P, mode, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(Y), bits(ref)), f"replay {r}"
 
 
 def test_noalloc_rejects_oversized_workspace():
