@@ -22,6 +22,8 @@ SHAPES = [
     (300, 1024, 1000, 8, True),     # ragged N tile (1000 = 7 x 128 + 104)
     (256, 256, 136, 2, False),
     (320, 512, 384, 1, True),       # P = 1: the plain GEMM
+    (256, 192, 256, 3, True),       # P = 3, K/P = 64: one K step per shard
+    (300, 4096, 200, 64, False),    # P = 64 (the most shards), K/P = 64, ragged M and N
 ]
 
 
