@@ -589,21 +589,35 @@ def main():
             st["frac_hbm_peak"] = st["gbps"] / PEAK_HBM_GBPS
         op_stats[name] = st
 
-    # Context, outside the timed step: each GEMM's shard 0 alone at its real
-    # shape, and a plain device copy of 1 GiB.
+    # Context, outside the timed step: each GEMM's shards alone at their real
+    # shape, in turn, and a plain device copy of 1 GiB.
+    # The launches are captured in a HIP graph and the replay is timed: a
+    # decode shard runs for ~10 us, less than one call from Python costs the
+    # host, so eager launches would time the host.
     single = {}
     for name, fl, nb, fns in wl.single:
-        for r in range(3):
-            fns[r % len(fns)]()
-        torch.cuda.synchronize()
         reps = max(10, len(fns))
+        seq = [fns[r % len(fns)] for r in range(reps)]
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for f in seq[:3]:
+                f()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        sgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(sgraph):
+            for f in seq:
+                f()
+        sgraph.replay()                 # one untimed replay
+        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        for r in range(reps):
-            fns[r % len(fns)]()
+        sgraph.replay()
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) / reps * 1e3
+        del sgraph
         single[name] = dict(avg_us=us, tflops=fl / us / 1e6,
                             frac_bf16_peak=fl / us / 1e6 / PEAK_BF16_TFLOPS)
         if nb:
@@ -664,7 +678,8 @@ def main():
                     "shader_clock_ghz": clocks,
                     "note": "one_shard: each GEMM's shards launched alone at their real shape "
                             "(one GPU's share), one after another (so a shard is not still "
-                            "cached from the launch before), and for the prefill workloads the whole row layer "
+                            "cached from the launch before), captured in a HIP graph and the replay timed, "
+                            "and for the prefill workloads the whole row layer "
                             "through TP_ROW_FUSED back to back (the fold inside the GEMM, bitwise equal to "
                             "partials + fold); device_copy_gbps: read+write bytes of a 1 GiB "
                             "device-to-device copy per second; shader_clock_ghz: the shader "
