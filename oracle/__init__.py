@@ -92,7 +92,7 @@ def widen_f32(a: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
-# O2: dense product.
+# Dense product.
 # ---------------------------------------------------------------------------
 
 def dense(X: np.ndarray, W_io: np.ndarray) -> np.ndarray:
@@ -112,7 +112,7 @@ def dense(X: np.ndarray, W_io: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
-# O3: explicit split into P shards ("模型并行", "Tensor-parallel 线性层":
+# Explicit split into P shards ("模型并行", "Tensor-parallel 线性层":
 # the split dim must divide evenly; shard i is the i-th contiguous chunk).
 # ---------------------------------------------------------------------------
 
@@ -133,7 +133,7 @@ def split(A: np.ndarray, P: int, dim: int) -> list:
 
 
 # ---------------------------------------------------------------------------
-# O4: column parallel.  O5: row parallel.
+# Column parallel and row parallel.
 # ---------------------------------------------------------------------------
 
 def column_shards(X: np.ndarray, W_io: np.ndarray, P: int) -> list:
@@ -169,7 +169,7 @@ def row_parallel_linear(X: np.ndarray, W_io: np.ndarray, P: int) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
-# O6: the fp32 shard fold and O9: bf16 rounding (bit-exact references).
+# The fp32 shard fold and bf16 rounding (bit-exact references).
 # ---------------------------------------------------------------------------
 
 def fold_f32(partials: np.ndarray, bias=None) -> np.ndarray:
@@ -203,7 +203,7 @@ def round_bf16(a: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
-# O7: reduce-scatter over tokens and the all-gather that undoes it.
+# Reduce-scatter over tokens and the all-gather that undoes it.
 # ---------------------------------------------------------------------------
 
 def reduce_scatter_rows(parts: list, P: int, fold=fold_f64) -> list:
@@ -282,7 +282,7 @@ def row_parallel_linear_bias(X: np.ndarray, W_io: np.ndarray, b, P: int) -> np.n
 
 def column_parallel_linear_gathered(slices: list, W_io: np.ndarray, P: int) -> np.ndarray:
     """The column layer of the sequence-parallel layout: the P token slices
-    are all-gathered (Shard(0) -> Replicate, O7) into the full X, which then
+    are all-gathered (Shard(0) -> Replicate) into the full X, which then
     goes through the column-parallel product (nanotron "5.1 TP", column
     REDUCE_SCATTER mode: all_gather(x) before F.linear)."""
     return column_parallel_linear(all_gather_rows(slices), W_io, P)
@@ -312,7 +312,7 @@ def embedding_parallel(ids, E: np.ndarray, P: int) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
-# O8: placements as integer index maps.
+# Placements as integer index maps.
 # ---------------------------------------------------------------------------
 
 REPLICATE, SHARD, PARTIAL = 0, 1, 2
@@ -322,7 +322,7 @@ def shard_index_sets(rows: int, cols: int, kind: int, dim: int, P: int) -> list:
     """For each of the P shards, the set of global (r, c) indices it holds.
 
     Shard(dim): the tensor is tagged with its flat global index and split
-    with the same explicit split as the data (O3); each shard holds the
+    with the same explicit split as the data (`split`); each shard holds the
     indices that land in its chunk.  Replicate() and Partial(): every shard
     holds the full index set (for Partial, a full-shape part of the sum).
     dim may be negative (counted from the last of the 2 dims).
@@ -371,7 +371,7 @@ def expected_views(rows: int, cols: int, ld: int, kind: int, dim: int, P: int) -
 
 
 # ---------------------------------------------------------------------------
-# O10: comparison metrics behind every tolerance bar (the page "模型并行",
+# Comparison metrics behind every tolerance bar (the page "模型并行",
 # section "Tensor-parallel 线性层", compares the sharded result with the dense
 # product element by element).
 # ---------------------------------------------------------------------------

@@ -316,7 +316,7 @@ def test_index_sets_cover_exactly_once(R, C):
 
 
 # ---------------------------------------------------------------------------
-# O10 metrics.  Every tolerance verdict goes through rel_l2 and max_abs, so
+# Comparison metrics.  Every tolerance verdict goes through rel_l2 and max_abs, so
 # they are pinned to values worked out by hand from their definitions:
 # rel_l2 = ||got - ref||_2 / ||ref||_2, max_abs = max |got - ref|.
 # ---------------------------------------------------------------------------
