@@ -295,7 +295,7 @@ hipError_t launch_gemm_skinny(const GemmArgs &g, int out_type, const FoldArgs *f
     if (exp) ex = *exp;
     if (ex.x_rows > 0) return hipErrorInvalidValue;
     // LDS per workgroup: NST * (16*NB + 16*MB) * KB * 2 bytes, plus the
-    // cross-wave sums.  Small stages let several workgroups share a CU, which
+    // cross-wave sums (4 * NB * MB KB).  Small stages let several workgroups share a CU, which
     // keeps more loads in flight when the grid is large (one workgroup per
     // 16 output columns and shard: three 16 KB stages, two in flight).  The
     // fused fold has a P times smaller grid: one workgroup per CU with 32
@@ -320,8 +320,23 @@ hipError_t launch_gemm_skinny(const GemmArgs &g, int out_type, const FoldArgs *f
         if (fold) return launch_mb<2, 1, 256, 4>(g, out_type, fold, ex, s);   // 96 KB
         return launch_mb<1, 1, 256, 3>(g, out_type, fold, ex, s);             // 48 KB
     }
-    if (g.M <= 32) return launch_mb<1, 2, 256, 2>(g, out_type, fold, ex, s);  // 48 KB
-    return launch_mb<1, 4, 256, 2>(g, out_type, fold, ex, s);                 // 80 KB
+    // Above 16 tokens every workgroup re-reads its X rows from L2 with each
+    // stage, so more W rows per workgroup share them (and no more 16-row X
+    // blocks than M needs).  Same-box sweep, 8 shards, us for M = 24 / 32 /
+    // 48 / 64, against 16 W rows per workgroup and 2 or 4 X blocks: column
+    // 4096 -> 28672: 39.9 / 39.1 / 55.9 / 72.2 vs 53.1 / 51.9 / 108.1 / 116.0;
+    // 8192 -> 10240: 33.8 / 35.2 / 43.0 / 67.8 vs 45.3 / 45.8 / 84.0 / 86.5;
+    // 8192 -> 28672: 88.4 / 88.4 / 103.2 / 145.6 vs 124.4 / 125.5 / 216.2 /
+    // 217.2; fused fold of 28672 -> 8192: 93.0 / 94.1 / 171.6 / 171.5 vs 119.8 /
+    // 123.5 / 228.7 / 230.5.  All bitwise equal (each output's K blocks and
+    // their order do not depend on the workgroup's shape).
+    if (g.M <= 32) {
+        if (fold) return launch_mb<4, 2, 256, 2>(g, out_type, fold, ex, s);   // 128 KB
+        return launch_mb<2, 2, 256, 2>(g, out_type, fold, ex, s);             // 80 KB
+    }
+    if (fold) return launch_mb<2, 4, 128, 3>(g, out_type, fold, ex, s);       // 104 KB
+    if (g.M <= 48) return launch_mb<4, 3, 256, 2>(g, out_type, fold, ex, s);  // 160 KB
+    return launch_mb<4, 4, 128, 2>(g, out_type, fold, ex, s);                 // 128 KB
 }
 
 }  // namespace tpl
