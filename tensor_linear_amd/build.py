@@ -23,7 +23,8 @@ CLOCK_LIB = os.path.join(HERE, "libtplclock.so")
 CLOCK_SOURCE = "clock_probe.hip"
 
 SOURCES = ["tplinear.cpp", "device.cpp", "gemm_tile.hip", "gemm_skinny.hip", "gemm_generic.hip",
-           "shard_fold.hip", "embedding.hip", "gemm_rowfold.hip", "noalloc.hip"]
+           "shard_fold.hip", "embedding.hip", "gemm_rowfold.hip", "gemm_narrow.hip",
+           "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -64,6 +64,11 @@ struct FoldArgs {
 hipError_t launch_gemm_tile(const GemmArgs &g, int out_type, const GemmExtra *ex,
                             hipStream_t s);
 bool gemm_tile_supported(const GemmArgs &g, const GemmExtra *ex);
+// 256 x 128 tiles, two waves per SIMD, for launches whose 256 x 256 tiles
+// would fill at most half of the CUs; no gated unit or token slices, and the
+// bias only with bf16 output.  Bitwise the same results as the tile kernel.
+hipError_t launch_gemm_narrow(const GemmArgs &g, int out_type, const GemmExtra *ex,
+                              hipStream_t s);
 
 // Skinny (M <= 64) bf16 kernel that streams W.  Requires K > 0, K % 8 == 0,
 // lda, ldb, a_shard, b_shard multiples of 8 and A, B 16-byte aligned.

@@ -14,6 +14,7 @@
 namespace tpl {
 // Reaching any of these means an argument check let a bad call through.
 hipError_t launch_gemm_tile(const GemmArgs &, int, const GemmExtra *, hipStream_t) { std::abort(); }
+hipError_t launch_gemm_narrow(const GemmArgs &, int, const GemmExtra *, hipStream_t) { std::abort(); }
 bool gemm_tile_supported(const GemmArgs &, const GemmExtra *) { std::abort(); }
 hipError_t launch_gemm_skinny(const GemmArgs &, int, const FoldArgs *, const GemmExtra *, hipStream_t) { std::abort(); }
 bool gemm_skinny_supported(const GemmArgs &, const GemmExtra *) { std::abort(); }

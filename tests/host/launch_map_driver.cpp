@@ -34,6 +34,7 @@ bool gemm_tile_supported(const GemmArgs &, const GemmExtra *) { return false; }
 bool gemm_skinny_supported(const GemmArgs &, const GemmExtra *) { return false; }
 bool gemm_rowfold_supported(const GemmArgs &, const ReduceArgs &) { return false; }
 hipError_t launch_gemm_tile(const GemmArgs &, int, const GemmExtra *, hipStream_t) { std::abort(); }
+hipError_t launch_gemm_narrow(const GemmArgs &, int, const GemmExtra *, hipStream_t) { std::abort(); }
 hipError_t launch_gemm_skinny(const GemmArgs &, int, const FoldArgs *, const GemmExtra *, hipStream_t) {
     std::abort();
 }

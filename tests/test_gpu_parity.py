@@ -92,10 +92,11 @@ ALIGNED = [
     (1, 512, 64, 8),
     (17, 256, 192, 4),             # skinny, two m-blocks, ragged M
     (64, 1024, 512, 2),            # skinny, four m-blocks
-    (65, 512, 512, 2),             # tile kernel, mostly-empty M tile
-    (300, 512, 2 * 300, 2),        # tile kernel, ragged M and N/P = 300
-    (512, 1024, 2048, 8),          # tile kernel, whole tiles
-    (256, 64 * 8, 256 * 8, 8),     # tile kernel, K/P = 64 (one K step)
+    (65, 512, 512, 2),             # few tiles: 256 x 128 kernel, mostly-empty M tile
+    (300, 512, 2 * 300, 2),        # 256 x 128 kernel, ragged M and N/P = 300
+    (512, 1024, 2048, 8),          # 256 x 128 kernel, whole tiles
+    (256, 64 * 8, 256 * 8, 8),     # 256 x 128 kernel, K/P = 64 (one K step)
+    (1100, 1024, 264 * 16, 16),    # 256 x 256 tile kernel (160 tiles), ragged M and N/P = 264
     (40, 24, 42, 3),               # skinny with K/P = 8 (K tail)
     (257, 72 * 2, 130, 2),         # generic (K/P = 72 is not a multiple of 64)
 ]
