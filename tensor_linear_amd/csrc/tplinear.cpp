@@ -66,8 +66,10 @@ int64_t view_stride(int64_t rows, int64_t cols, int64_t ld, int32_t kind, int32_
 
 // Run one grouped shard GEMM with the best kernel that takes it.
 // Decode-shaped bf16 problems (M <= 64) stream W with the skinny kernel;
-// large aligned bf16 problems use the 256x256 MFMA tile kernel; everything
-// else (fp32, odd K, unaligned views) uses the generic kernel.
+// aligned bf16 problems use the 256x256 MFMA tile kernel, or its 256x128
+// two-waves-per-SIMD form when the 256x256 tiles would fill at most half of
+// the CUs; everything else (fp32, odd K, unaligned views) uses the generic
+// kernel.
 hipError_t run_gemm(const GemmArgs &g, int32_t dtype, int out_type, const GemmExtra *ex,
                     hipStream_t s) {
     if (dtype == TP_BF16) {
