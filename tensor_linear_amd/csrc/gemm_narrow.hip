@@ -1,21 +1,28 @@
-// Column shard GEMM (and row partials) on 256 x 128 output tiles with two
-// waves per SIMD, for launches whose 256 x 256 tiles would fill at most half
-// of the CUs ("模型并行", "Tensor Parallel": the per-shard products Y_i =
-// X W_i and X_i W_i).  Eight waves in a 4 x 2 grid, each a 64 x 64 block of
-// 4 x 4 v_mfma_f32_16x16x32_bf16 blocks, the instruction and the K order of
-// the 256 x 256 tile kernel, so every output is bitwise the same; half-width
-// tiles give twice the workgroups, and the second wave on each SIMD issues
-// its MFMAs while the first waits on its LDS reads and loads.
+// Column shard GEMM (and row partials) on narrow output tiles, for launches
+// whose 256 x 256 tiles would fill at most half of the CUs ("模型并行",
+// "Tensor Parallel": the per-shard products Y_i = X W_i and X_i W_i).  Each
+// wave owns a 64 x 64 block of 4 x 4 v_mfma_f32_16x16x32_bf16 blocks, with
+// the instruction and the K order of the 256 x 256 tile kernel, so every
+// output is bitwise the same.  Two tile heights:
+//  - 128 x 128 tiles, four waves in a 2 x 2 grid, when they fit in one pass
+//    over the CUs (up to 128 tokens, and up to 256 when the N side is short):
+//    no MFMA work on rows past M, twice the workgroups of 256-row tiles
+//    where M > 128;
+//  - else 256 x 128 tiles, eight waves in a 4 x 2 grid, two per SIMD: the
+//    second wave on each SIMD issues its MFMAs while the first waits on its
+//    LDS reads and loads.
 //
 // Pipeline (the fold-in-registers kernel's eight-wave form, without the
-// fold): three stages of 64 K columns for both operands (3 x (32 + 16) KB),
-// 128-byte LDS rows with 16-byte chunk c of row r at slot c ^ ((r / 2) % 8),
-// global -> LDS with global_load_lds_dwordx4.  Per K step each wave issues
-// 32 MFMAs in two substeps of 32 K: during substep 0 it reads its substep-1
-// fragments and issues all 6 of step it+2's loads into the stage step it-1
-// freed; then the step's one barrier; during substep 1 it reads the next
-// step's substep-0 fragments.  Persistent workgroups walk an XCD-contiguous
-// range of (shard, tile) pairs; the K pipeline runs across tiles.
+// fold): three stages of 64 K columns for both operands (3 x (32 + 16) KB,
+// or 3 x (16 + 16) KB for 128 rows), 128-byte LDS rows with 16-byte chunk c
+// of row r at slot c ^ ((r / 2) % 8), global -> LDS with
+// global_load_lds_dwordx4.  Per K step each wave issues 32 MFMAs in two
+// substeps of 32 K: during substep 0 it reads its substep-1 fragments and
+// issues all of step it+2's loads (6 per wave with 256 rows, 8 with 128)
+// into the stage step it-1 freed; then the step's one barrier; during
+// substep 1 it reads the next step's substep-0 fragments.  Persistent
+// workgroups walk an XCD-contiguous range of (shard, tile) pairs; the K
+// pipeline runs across tiles.
 #include "kernels.h"
 
 namespace tpl {
@@ -26,10 +33,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_PTR(T) __attribute__((address_space(3))) T *
 
-constexpr int FM = 256;   // tile rows (tokens)
 constexpr int FN = 128;   // tile columns (output features)
-constexpr int NT = 512;   // threads: 8 waves, two per SIMD
-constexpr int NW = NT / 64;
 constexpr int FBK = 64;   // K columns per stage
 constexpr int FGROUP = 4; // tile rows visited as a group
 
@@ -67,16 +71,19 @@ __device__ __forceinline__ int narrow_tile_of(const NarrowSched &ts, int q) {
     return t < ts.T ? t : -1;
 }
 
-template <int OUT>
-__global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
+// FM: tile rows, 256 (eight waves, two per SIMD) or 128 (four waves).
+template <int OUT, int FM>
+__global__ __attribute__((amdgpu_flat_work_group_size(FM * 2, FM * 2),
+                          amdgpu_waves_per_eu(FM / 128, FM / 128)))
 void gemm_narrow_kernel(GemmArgs g, NarrowSched ts, const __bf16 *bias_all, int64_t bias_shard,
                         int vec_store) {
+    constexpr int NW = FM / 32;            // waves
     constexpr int ROWB = FBK * 2;          // 128 bytes per LDS row
-    constexpr int OPX = FM * ROWB;         // X stage, 32 KB
+    constexpr int OPX = FM * ROWB;         // X stage, 32 or 16 KB
     constexpr int OPW = FN * ROWB;         // W stage, 16 KB
     constexpr int W_BASE = 3 * OPX;        // three X stages, then three W stages
     constexpr int LX = OPX / 1024 / NW;    // X loads per wave per step (4)
-    constexpr int LW = OPW / 1024 / NW;    // W loads per wave per step (2)
+    constexpr int LW = OPW / 1024 / NW;    // W loads per wave per step (2 or 4)
     __shared__ __attribute__((aligned(1024))) char smem[3 * OPX + 3 * OPW];
     LDS_PTR(char) lds = (LDS_PTR(char))smem;
     const uint32_t lds_u = (uint32_t)(uintptr_t)lds;
@@ -143,8 +150,8 @@ void gemm_narrow_kernel(GemmArgs g, NarrowSched ts, const __bf16 *bias_all, int6
         asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                      :: "v"(voff), "s"(base), "s"(lds_addr) : "memory", "m0");
     };
-    // Load l (0..5) of the cursor's step into stage `slot`: 0..3 the X tile
-    // (1 KB chunks 8l + wave), 4..5 the W tile.
+    // Load l (0 .. LX+LW-1) of the cursor's step into stage `slot`: the
+    // first LX the X tile (1 KB chunks NW*l + wave), then the W tile.
     auto load = [&](int slot, int l) __attribute__((always_inline)) {
         if (l < LX)
             dma(pa + (int64_t)pkt * 128, aoff[l], lds_u + slot * OPX + (l * NW + wave) * 1024);
@@ -206,15 +213,17 @@ void gemm_narrow_kernel(GemmArgs g, NarrowSched ts, const __bf16 *bias_all, int6
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[0][i], fr[0][4 + j], acc[i][j], 0, 0, 0);
                     const bool rd = (u & 1) == 0;
                     if (rd) read_frag(1, u >> 1, frag_addr(s0, u >> 1, 1));
-                    // step it+2's six loads, X then W, at MFMAs 1, 3, 6, 9, 11, 14
-                    const int li = u == 1 ? 0 : u == 3 ? 1 : u == 6 ? 2 : u == 9 ? 3 : u == 11 ? 4 : u == 14 ? 5 : -1;
+                    // step it+2's loads, X then W: six at MFMAs 1, 3, 6, 9,
+                    // 11, 14 (256 rows) or eight at the odd MFMAs (128 rows)
+                    const int li = LX + LW == 8 ? ((u & 1) ? (u >> 1) : -1)
+                                 : u == 1 ? 0 : u == 3 ? 1 : u == 6 ? 2 : u == 9 ? 3 : u == 11 ? 4 : u == 14 ? 5 : -1;
                     if (li >= 0) load(s2, li);
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
                     if (rd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 // Step it+1's loads (issued in step it-1) have landed; step
-                // it+2's 6 may stay in flight.  This wave's reads of
+                // it+2's may stay in flight.  This wave's reads of
                 // step it's stage are done before anyone's loads may
                 // overwrite it (two steps on).  After an epilogue its stores
                 // are in flight too, and a store may complete before an
@@ -249,7 +258,7 @@ void gemm_narrow_kernel(GemmArgs g, NarrowSched ts, const __bf16 *bias_all, int6
         // ---- epilogue: acc (+ bias) -> the output type.  acc[i][j][r] =
         // C[m = 16j + lane%16][n = 16i + 4*(lane/16) + r] of the wave's block.
         // 16 rows x 64 columns at a time go through this wave's 1 KB chunks
-        // w + 8c (c = 0..3) of the X stage of the tile's last step (read by
+        // w + NW*c (c = 0..3) of the X stage of the tile's last step (read by
         // everyone before that step's barrier; only this wave's own later
         // loads write these chunks): staging row r of 256 bytes at chunk r/4,
         // offset (r%4)*256, 16-byte slot s at s ^ (r % 16).  Then each lane
@@ -334,10 +343,6 @@ inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 }  // namespace
 
-int64_t gemm_narrow_tiles(const GemmArgs &g) {
-    return ((g.M + FM - 1) / FM) * ((g.N + FN - 1) / FN) * g.P;
-}
-
 hipError_t launch_gemm_narrow(const GemmArgs &g, int out_type, const GemmExtra *exp,
                               hipStream_t s) {
     if (g.M == 0 || g.N == 0 || g.P == 0) return hipSuccess;
@@ -345,24 +350,38 @@ hipError_t launch_gemm_narrow(const GemmArgs &g, int out_type, const GemmExtra *
     if (exp) ex = *exp;
     if (ex.act != ACT_NONE || ex.x_rows > 0 || (out_type != OUT_BF16 && ex.bias))
         return hipErrorInvalidValue;
-    const int64_t tm = (g.M + FM - 1) / FM, tn = (g.N + FN - 1) / FN;
+    // 128-row tiles when they fit in one pass over the CUs, else 256-row.
+    // Same-box A/B, 8 shards, us after a read-only 1 GiB cache flush / warm,
+    // 128-row vs 256-row tiles: M = 128, 4096 -> 28672: 61.6 / 41.0 vs
+    // 65.5 / 56.9; M = 65, 8192 -> 10240: 74.2 / 54.6 vs 91.7 / 88.3;
+    // M = 256, 8192 -> 10240: 83.9 / 62.0 vs 110.7 / 88.6; M = 200,
+    // 4096 -> 14336: 49.0 / 41.6 vs 57.6 / 49.4.  Bitwise equal.
+    const int cus = device_cu_count();
+    const int64_t tn = (g.N + FN - 1) / FN;
+    const int FM = ((g.M + 127) / 128) * tn * g.P <= cus ? 128 : 256;
+    const int64_t tm = (g.M + FM - 1) / FM;
     const int64_t T = tm * tn * g.P;
     if (T > 0x7FFFFFFFll) return hipErrorInvalidConfiguration;
     NarrowSched ts;
     ts.tiles_m = (int)tm;
     ts.tiles_n = (int)tn;
     ts.T = (int)T;
-    const int cus = device_cu_count();
     const int grid = (int)(T < cus ? T : cus);
     ts.xcd_split = (grid == cus && cus % 8 == 0 && T >= cus) ? 1 : 0;
     ts.per_xcd = grid / 8;
     const int vw = out_type == OUT_BF16 ? 8 : 4;
     const int vec = g.ldc % vw == 0 && g.c_shard % vw == 0 && aligned16(g.C);
     const __bf16 *bias = (const __bf16 *)ex.bias;
-    if (out_type == OUT_BF16)
-        gemm_narrow_kernel<OUT_BF16><<<dim3(grid), dim3(NT), 0, s>>>(g, ts, bias, ex.bias_shard, vec);
-    else
-        gemm_narrow_kernel<OUT_F32><<<dim3(grid), dim3(NT), 0, s>>>(g, ts, nullptr, 0, vec);
+    if (FM == 128) {
+        if (out_type == OUT_BF16)
+            gemm_narrow_kernel<OUT_BF16, 128><<<dim3(grid), dim3(256), 0, s>>>(g, ts, bias, ex.bias_shard, vec);
+        else
+            gemm_narrow_kernel<OUT_F32, 128><<<dim3(grid), dim3(256), 0, s>>>(g, ts, nullptr, 0, vec);
+    } else if (out_type == OUT_BF16) {
+        gemm_narrow_kernel<OUT_BF16, 256><<<dim3(grid), dim3(512), 0, s>>>(g, ts, bias, ex.bias_shard, vec);
+    } else {
+        gemm_narrow_kernel<OUT_F32, 256><<<dim3(grid), dim3(512), 0, s>>>(g, ts, nullptr, 0, vec);
+    }
     return hipGetLastError();
 }
 

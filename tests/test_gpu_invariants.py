@@ -29,13 +29,15 @@ pytestmark = pytest.mark.gpu
 
 # (label, M, K, N, P, dtype): each reaches a different kernel for the column
 # and/or the row GEMM (K/P, M and the tile count decide: skinny for M <= 64,
-# for K/P % 64 == 0 the 256 x 128 kernel when the 256 x 256 tiles would fill
-# at most half of the CUs and the 256 x 256 tile kernel otherwise, the generic
-# kernel for other K and for fp32).  Column P shards against P = 1 compares
-# the two MFMA kernels with each other on "tile-ragged".
+# for K/P % 64 == 0 the narrow kernel when the 256 x 256 tiles would fill at
+# most half of the CUs -- 128 x 128 tiles when those fit in one pass, else
+# 256 x 128 -- and the 256 x 256 tile kernel otherwise, the generic kernel
+# for other K and for fp32).  Column P shards against P = 1 compares the
+# 256 x 256 tile kernel with the 256 x 128 narrow tiles on "tile-ragged".
 SHAPES = [
-    ("narrow", 300, 1024, 1024, 8, "bf16"),          # few tiles: 256 x 128 tiles
+    ("narrow", 300, 1024, 1024, 8, "bf16"),          # few tiles: 128 x 128 tiles
     ("narrow-ragged", 257, 512, 520, 4, "bf16"),
+    ("narrow256", 520, 1024, 2048, 4, "bf16"),       # row partials of 4 shards: 256 x 128 tiles
     ("tile-ragged", 1100, 1024, 4224, 16, "bf16"),   # 160 / 1360 256 x 256 tiles
     ("skinny-m1", 1, 2048, 1000, 8, "bf16"),
     ("skinny-m16", 16, 4160, 1000, 8, "bf16"),   # K/P = 520: ragged last stage
