@@ -165,21 +165,25 @@ tp_status tp_linear_column(const void *X, int64_t ldx, const void *W, int64_t ld
  *   fold inside the GEMM where that is faster: each workgroup computes all P
  *   shard partials of its output tile in ascending order and adds them into
  *   a running fp32 sum, so no partial reaches memory and the workspace is
- *   not touched.  That holds for bf16 operands (16-byte aligned, leading
+ *   not touched.  Kernels exist for bf16 operands (16-byte aligned, leading
  *   dims and shard offsets multiples of 8) with 1 <= M <= 64, or with K/P a
- *   multiple of 64 and at most 2048 (at most 3584 when M*N >= 4096*4096),
- *   where the in-register fold measured faster.  Other shapes run the
- *   TP_ROW_SUM sequence in the workspace, which is therefore always
- *   required.
+ *   multiple of 64 and at most 2048 (at most 3584 when M*N >= 4096*4096);
+ *   they are used where they measured faster: for M <= 16 when N >= 32 x the
+ *   GPU's CU count and K/P >= 2048, or N is smaller and K/P <= 1024; for
+ *   M > 64 when the output has at least CUs * min(1, (K/P + 512) / 2048)
+ *   tiles of 256 x 128.  Other shapes run the TP_ROW_SUM sequence in the
+ *   workspace, which is therefore always required.  With the environment
+ *   variable TPLINEAR_ROW_FOLD=gemm every shape a fused kernel takes runs
+ *   it (same result).
  * mode TP_ROW_SCATTER: requires M % P == 0.  Token slice j = rows
  *   [j*M/P, (j+1)*M/P) of the fold is written to Y + j*y_slice_stride with
  *   row stride ldy (y_slice_stride = 0 means (M/P)*ldy, the contiguous layout
  *   whose Shard(0) views are the slices; a nonzero stride must be at least
  *   (M/P - 1)*ldy + N, so that slices do not overlap, else TP_ERR_SHAPE).
  *   The reduce-scatter over tokens.
- *   Bit for bit the rows of TP_ROW_SUM; for bf16 with K/P as for
- *   TP_ROW_FUSED and M/P a multiple of 256 the fold runs inside the GEMM and
- *   the workspace is not touched.
+ *   Bit for bit the rows of TP_ROW_SUM; for bf16 with K/P and the tile
+ *   count as for TP_ROW_FUSED with M > 64, and M/P a multiple of 256, the
+ *   fold runs inside the GEMM and the workspace is not touched.
  * y_slice_stride is ignored by the other modes.
  * workspace: device memory of ws_bytes >= tp_row_workspace_bytes(mode, M, N, P),
  *   256-byte aligned.  May be NULL when that size is 0.  Calls that share a
@@ -335,14 +339,16 @@ tp_status tp_embedding(const int64_t *ids, int64_t T, const void *E,
  * GPU, kept until the process ends).  The call allocates nothing and calls no
  * allocating routine; the array's device address on the current device is
  * looked up once per device, on its first call there.
- * Limit: the calls that fold fp32 partials in a separate kernel --
- *   TP_ROW_SUM, and TP_ROW_FUSED / TP_ROW_SCATTER at the shapes where the
- *   fold does not run inside the GEMM (see TP_ROW_FUSED) -- need
+ * Limit: the calls that fold fp32 partials in a separate kernel need
  *   tp_row_workspace_bytes(mode, M, N, P) <= TP_NOALLOC_SCRATCH_BYTES, else
- *   TP_ERR_WORKSPACE before anything is queued; TP_ROW_PARTIAL and the
- *   calls whose fold runs inside the GEMM use no workspace and have no such
- *   limit.  No part of the array has to start at zero: every partial is
- *   written before the fold reads it.
+ *   TP_ERR_WORKSPACE before anything is queued: TP_ROW_SUM, and TP_ROW_FUSED
+ *   / TP_ROW_SCATTER at the shapes no fused kernel takes (see TP_ROW_FUSED;
+ *   where the partials would not fit the array, these two modes fold inside
+ *   the GEMM at every shape a fused kernel takes, as with
+ *   TPLINEAR_ROW_FOLD=gemm).  TP_ROW_PARTIAL and the calls whose fold runs
+ *   inside the GEMM use no workspace and have no such limit.  No part of the
+ *   array has to start at zero: every partial is written before the fold
+ *   reads it.
  * Concurrency: all calls on one GPU share that GPU's array and it keeps the
  *   last call's contents, so calls that may overlap on one GPU (on different
  *   streams without ordering, or from several threads) race on it and must

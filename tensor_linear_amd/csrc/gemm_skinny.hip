@@ -299,7 +299,8 @@ hipError_t launch_gemm_skinny(const GemmArgs &g, int out_type, const FoldArgs *f
     // keeps more loads in flight when the grid is large (one workgroup per
     // 16 output columns and shard: three 16 KB stages, two in flight).  The
     // fused fold has a P times smaller grid: one workgroup per CU with 32
-    // output columns and four 24 KB stages, three in flight.  Measured with
+    // output columns and four 24 KB stages, three in flight (16 columns and
+    // four 16 KB stages where 32 would leave CUs without one).  Measured with
     // M = 16, K = 8192, N = 28672 over 8 shards: column 82-83 us with 3 or 4
     // stages of 256 columns against 88-89 with 2; fused fold of 8 shards of
     // K = 3584, N = 8192: 82-83 us with 32 columns and 3-6 stages, 86-87 with
@@ -317,7 +318,14 @@ hipError_t launch_gemm_skinny(const GemmArgs &g, int out_type, const FoldArgs *f
         return launch_mb<2, 4, 256, 2, true>(g, out_type, fold, ex, s);                  // 96 KB
     }
     if (g.M <= 16) {
-        if (fold) return launch_mb<2, 1, 256, 4>(g, out_type, fold, ex, s);   // 96 KB
+        // Fused fold: 32 output columns per workgroup where that still gives
+        // every CU one, else 16.  Same box, 8 shards, us after a read-only
+        // 1 GiB flush, 16 vs 32 columns: 4096 -> 4096 13.8 vs 16.3-16.8,
+        // 8192 -> 4096 21.2-21.6 vs 26.0-26.1, 14336 -> 4096 31.8-32.2 vs
+        // 38.6-39.4; bitwise equal.
+        if (fold && g.N >= 32 * (int64_t)device_cu_count())
+            return launch_mb<2, 1, 256, 4>(g, out_type, fold, ex, s);         // 96 KB
+        if (fold) return launch_mb<1, 1, 256, 4>(g, out_type, fold, ex, s);   // 64 KB
         return launch_mb<1, 1, 256, 3>(g, out_type, fold, ex, s);             // 48 KB
     }
     // Above 16 tokens every workgroup re-reads its X rows from L2 with each

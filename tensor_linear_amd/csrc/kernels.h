@@ -142,10 +142,13 @@ struct RowPlan {
     GemmArgs g; ReduceArgs r; FoldArgs f; GemmExtra ex;
     int out; int32_t dtype;
 };
+// ws_cap: the workspace bytes the caller can give; where the P fp32 partials
+// would not fit it, TP_ROW_FUSED / TP_ROW_SCATTER fold inside the GEMM
+// wherever a kernel takes the shape.
 tp_status plan_row(const void *X, int64_t ldx, const void *W, int64_t ldw, const void *bias,
                    void *Y, void *const *y_slices, int64_t ldy, int64_t y_slice_stride,
                    int32_t mode, int64_t M, int64_t N, int64_t K, int32_t P, int32_t dtype,
-                   RowPlan &plan);
+                   size_t ws_cap, RowPlan &plan);
 // Queue the plan's kernels; `workspace` is read only by PARTIALS_AND_FOLD
 // (TP_ERR_WORKSPACE if it is null there).
 tp_status run_row(RowPlan &plan, float *workspace, hipStream_t s);

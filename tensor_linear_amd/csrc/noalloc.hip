@@ -60,7 +60,7 @@ extern "C" tp_status tp_linear_row_noalloc(const void *X, int64_t ldx, const voi
     if (M == 0 || N == 0) return TP_OK;
     tpl::RowPlan plan;
     const tp_status pst = tpl::plan_row(X, ldx, W, ldw, nullptr, Y, nullptr, ldy, y_slice_stride,
-                                        mode, M, N, K, P, dtype, plan);
+                                        mode, M, N, K, P, dtype, TP_NOALLOC_SCRATCH_BYTES, plan);
     if (pst != TP_OK) return pst;
     // Only the partials-and-fold path uses a workspace: the P fp32 partials.
     void *ws = nullptr;

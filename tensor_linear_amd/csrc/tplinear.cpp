@@ -5,6 +5,11 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+
 #include "kernels.h"
 
 namespace {
@@ -66,20 +71,22 @@ int64_t view_stride(int64_t rows, int64_t cols, int64_t ld, int32_t kind, int32_
 
 // Run one grouped shard GEMM with the best kernel that takes it.
 // Decode-shaped bf16 problems (M <= 64) stream W with the skinny kernel;
-// aligned bf16 problems use the 256x256 MFMA tile kernel, or its 256x128
-// two-waves-per-SIMD form when the 256x256 tiles would fill at most half of
-// the CUs; everything else (fp32, odd K, unaligned views) uses the generic
-// kernel.
+// aligned bf16 problems use the 256x256 MFMA tile kernel, or its narrow
+// forms (128x128, or 256x128 with two waves per SIMD) when the 256x256
+// tiles would fill at most half of the CUs; everything else (fp32, odd K,
+// unaligned views) uses the generic kernel.
 hipError_t run_gemm(const GemmArgs &g, int32_t dtype, int out_type, const GemmExtra *ex,
                     hipStream_t s) {
     if (dtype == TP_BF16) {
         if (gemm_skinny_supported(g, ex)) return launch_gemm_skinny(g, out_type, nullptr, ex, s);
         if (gemm_tile_supported(g, ex)) {
-            // Few 256 x 256 tiles (short prompts): half-width tiles with two
-            // waves per SIMD.  Same-box times, 8 shards, cold / warm: M = 128,
-            // 4096 -> 28672: 93.9 / 53.5 vs 106.3 / 78.0 us; M = 128, 8192 ->
-            // 10240: 123.5 / 82.9 vs 168.9 / 133.3 us; M = 256, 4096 -> 28672:
-            // 114.7 / 53.1 vs 123.7 / 74.9 us.
+            // Few 256 x 256 tiles (short prompts): the narrow kernel.  Its
+            // 256 x 128 form against the 256 x 256 tiles, same-box times, 8
+            // shards, after a 1 GiB write / warm: M = 128, 4096 -> 28672:
+            // 93.9 / 53.5 vs 106.3 / 78.0 us; M = 128, 8192 -> 10240: 123.5 /
+            // 82.9 vs 168.9 / 133.3 us; M = 256, 4096 -> 28672: 114.7 / 53.1
+            // vs 123.7 / 74.9 us (its 128 x 128 form is faster again where
+            // those tiles fit in one pass).
             const bool plain = !ex || (ex->act == ACT_NONE && ex->x_rows == 0 &&
                                        (out_type == OUT_BF16 || !ex->bias));
             const int64_t t256 = ((g.M + 255) / 256) * ((g.N + 255) / 256) * g.P;
@@ -269,12 +276,53 @@ tp_status row_args_status(const void *X, int64_t ldx, const void *W, int64_t ldw
     return TP_OK;
 }
 
+// TPLINEAR_ROW_FOLD=gemm: TP_ROW_FUSED and TP_ROW_SCATTER fold inside the
+// GEMM wherever a kernel takes the shape, not only where that measured
+// faster (the result is the same, bit for bit).
+bool row_fold_in_gemm_forced() {
+    const char *e = getenv("TPLINEAR_ROW_FOLD");
+    return e && strcmp(e, "gemm") == 0;
+}
+
+// The two ways to fold give the same bits, so the choice is by speed alone.
+// Same-box times, 8 shards, bf16, us after a read-only 1 GiB flush (warm in
+// brackets), partials + fold vs the fold inside the GEMM:
+// Decode (M <= 64, the skinny kernel): above 16 tokens the fused form loses
+// everywhere (M = 32: 4096 x 14336 -> 4096 33.5 vs 83.1, 8192 -> 8192 38.2 vs
+// 51.8, 28672 -> 8192 100.2 vs 179.7; M = 64: 51.4 vs 92.7, 58.9 vs 60.1,
+// 155.3 vs 175.8).  Up to 16 tokens it wins where its grid fills the CUs
+// with 32 output columns per workgroup and the shard's K is long (28672 ->
+// 8192, M = 16: 91.3 vs 95.5; 57344 -> 8192: 155.8 vs 178.3), or where 16
+// columns per workgroup fill them and the layer is small (4096 -> 4096:
+// 13.8 vs 17.1; 8192 -> 4096: 21.2 vs 22.4), and loses otherwise (8192 ->
+// 8192, K/P = 1024: 34.1-35.1 vs 31.5-33.8; 14336 -> 4096, K/P = 1792:
+// 31.8-32.2 vs 29.4-33.0 [26.0-26.4 vs 31.8-32.0]).
+bool skinny_fold_faster(int64_t M, int64_t N, int64_t Ks) {
+    if (M > 16) return false;
+    return N >= 32 * (int64_t)device_cu_count() ? Ks >= 2048 : Ks <= 1024;
+}
+
+// Prefill (M > 64, the 256 x 128 fold-in-registers kernel): it walks the P
+// shards of each output tile in turn, so it needs enough tiles; the shorter
+// the shard's K, the fewer.  Crossovers (tiles: fused vs unfused): K/P = 512,
+// 4096 -> 4096: 64 tiles 60.5 vs 41.8, 96 59.0 vs 61.0, 128 59.5 vs 75.7;
+// K/P = 1024, 8192 -> 8192: 128 110.3 vs 98.1 [91.0 vs 93.5], 192 111.6 vs
+// 143.7; 8192 -> 4096: 128 110.2 vs 96.4, 192 109.5 vs 141.1; K/P = 1792,
+// 14336 -> 4096: 128 193.5 vs 131.6, 192 197.1 vs 189.9 [157.9 vs 178.7],
+// 256 201.7 vs 242.0; K/P = 2048, 16384 -> 8192: 192 241.3 vs 212.1, 256
+// 228.9 vs 282.3.  So: tiles >= CUs * min(1, (K/P + 512) / 2048).
+bool rowfold_faster(int64_t M, int64_t N, int64_t Ks) {
+    if (M <= 64) return false;
+    const int64_t tiles = ((M + 255) / 256) * ((N + 127) / 128);
+    return tiles * 2048 >= (int64_t)device_cu_count() * std::min<int64_t>(2048, Ks + 512);
+}
+
 // The kernels tp_linear_row_ex runs for a call that passed
 // row_args_status (non-empty), and whether they use the workspace.
 tp_status plan_row(const void *X, int64_t ldx, const void *W, int64_t ldw, const void *bias,
                    void *Y, void *const *y_slices, int64_t ldy, int64_t y_slice_stride,
                    int32_t mode, int64_t M, int64_t N, int64_t K, int32_t P, int32_t dtype,
-                   RowPlan &p) {
+                   size_t ws_cap, RowPlan &p) {
     const int64_t Ks = K / P;
     // Shard strides from the placements: X [M, K] and W [N, K] Shard(1)
     // (column blocks); the partials Partial() (P [M, N] buffers back to
@@ -304,7 +352,11 @@ tp_status plan_row(const void *X, int64_t ldx, const void *W, int64_t ldw, const
     if (p_stride < 0) return TP_ERR_SHAPE;
     g.C = nullptr; g.ldc = N; g.c_shard = p_stride;   // the workspace, set by run_row
 
-    if (mode == TP_ROW_FUSED && dtype == TP_BF16 && gemm_skinny_supported(g, nullptr)) {
+    // Fold inside the GEMM where a kernel takes the shape and that is the
+    // faster way, or the override asks for it, or the partials would not fit.
+    const bool any_fold = row_fold_in_gemm_forced() || partials_bytes(M, N, P) > ws_cap;
+    if (mode == TP_ROW_FUSED && dtype == TP_BF16 && gemm_skinny_supported(g, nullptr) &&
+        (any_fold || skinny_fold_faster(M, N, Ks))) {
         p.f.Y = Y; p.f.ldy = ldy; p.f.out_type = p.out;
         p.path = RowPlan::SKINNY_FOLD;
         return TP_OK;
@@ -335,7 +387,7 @@ tp_status plan_row(const void *X, int64_t ldx, const void *W, int64_t ldw, const
     // 0.93, 7168 1.04; 16384 x 8192: 3584 0.92, 7168 1.02.
     const bool fold_in_gemm = Ks <= 2048 || (Ks <= 3584 && M * N >= (int64_t)4096 * 4096);
     if ((mode == TP_ROW_FUSED || mode == TP_ROW_SCATTER) && dtype == TP_BF16 && fold_in_gemm &&
-        gemm_rowfold_supported(g, r)) {
+        gemm_rowfold_supported(g, r) && (any_fold || rowfold_faster(M, N, Ks))) {
         p.path = RowPlan::ROWFOLD;
         return TP_OK;
     }
@@ -381,7 +433,7 @@ tp_status tp_linear_row_ex(const void *X, int64_t ldx, const void *W, int64_t ld
         return TP_ERR_WORKSPACE;
     RowPlan plan;
     const tp_status pst = plan_row(X, ldx, W, ldw, bias, Y, y_slices, ldy, y_slice_stride, mode,
-                                   M, N, K, P, dtype, plan);
+                                   M, N, K, P, dtype, SIZE_MAX, plan);
     if (pst != TP_OK) return pst;
     return run_row(plan, (float *)workspace, (hipStream_t)stream);
 }

@@ -1,5 +1,8 @@
 """Helpers shared by the GPU tests: moving seeded inputs to the device and
 results back.  No arithmetic of the method lives here."""
+import contextlib
+import os
+
 import numpy as np
 import torch
 
@@ -55,3 +58,26 @@ def workspace(mode, M, N, P, zero=True) -> torch.Tensor:
 def bf16_tol(K: int, sx: float = 1.0, sw: float = 0.02) -> float:
     """Max-abs bar for bf16 inputs with fp32 accumulation: 2e-2 sqrt(K) sx sw."""
     return 2e-2 * np.sqrt(K) * sx * sw
+
+
+# The two choices of the fused row modes: the library's own (the fold inside
+# the GEMM only where that measured faster) and every shape a fused kernel
+# takes (TPLINEAR_ROW_FOLD=gemm).  Both give the bits of TP_ROW_SUM.
+FOLD_POLICIES = (None, "gemm")
+
+
+@contextlib.contextmanager
+def row_fold(policy):
+    """Run the calls inside with TPLINEAR_ROW_FOLD = policy (None: unset)."""
+    old = os.environ.get("TPLINEAR_ROW_FOLD")
+    if policy is None:
+        os.environ.pop("TPLINEAR_ROW_FOLD", None)
+    else:
+        os.environ["TPLINEAR_ROW_FOLD"] = policy
+    try:
+        yield
+    finally:
+        if old is None:
+            os.environ.pop("TPLINEAR_ROW_FOLD", None)
+        else:
+            os.environ["TPLINEAR_ROW_FOLD"] = old

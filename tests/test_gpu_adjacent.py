@@ -25,7 +25,8 @@ import torch
 import oracle
 import synth
 import tensor_linear_amd as tl
-from gpu_util import DEV, bf16_dev, f32_dev, to_f64, bits, expected_bits, workspace, bf16_tol
+from gpu_util import (DEV, FOLD_POLICIES, bf16_dev, f32_dev, to_f64, bits, expected_bits, row_fold,
+                      workspace, bf16_tol)
 
 pytestmark = pytest.mark.gpu
 
@@ -112,15 +113,17 @@ def test_row_bias_bitwise(case):
     Xd, Wd, bd = _dev(X, dtype), _dev(W, dtype), _dev(b, dtype)
     X64, Wio = X.astype(np.float64), W.T.astype(np.float64)
     ref = oracle.row_parallel_linear_bias(X64, Wio, b.astype(np.float64), P)
-    for mode in (tl.TP_ROW_SUM, tl.TP_ROW_FUSED):
-        Y = torch.full((M, N), float("nan"), dtype=dtype, device=DEV)
-        tl.tp_linear_row_ex(Xd, Wd, Y, P, mode, workspace(mode, M, N, P), bias=bd)
-        assert np.array_equal(bits(Y), expected_bits(ref, dtype)), f"mode {mode}"
-    if M % P == 0:
-        Y = torch.full((M, N), float("nan"), dtype=dtype, device=DEV)
-        tl.tp_linear_row_ex(Xd, Wd, Y, P, tl.TP_ROW_SCATTER,
-                            workspace(tl.TP_ROW_SCATTER, M, N, P), bias=bd)
-        assert np.array_equal(bits(Y), expected_bits(ref, dtype)), "scatter"
+    for policy in FOLD_POLICIES:
+        with row_fold(policy):
+            for mode in (tl.TP_ROW_SUM, tl.TP_ROW_FUSED):
+                Y = torch.full((M, N), float("nan"), dtype=dtype, device=DEV)
+                tl.tp_linear_row_ex(Xd, Wd, Y, P, mode, workspace(mode, M, N, P), bias=bd)
+                assert np.array_equal(bits(Y), expected_bits(ref, dtype)), f"mode {mode} {policy}"
+            if M % P == 0:
+                Y = torch.full((M, N), float("nan"), dtype=dtype, device=DEV)
+                tl.tp_linear_row_ex(Xd, Wd, Y, P, tl.TP_ROW_SCATTER,
+                                    workspace(tl.TP_ROW_SCATTER, M, N, P), bias=bd)
+                assert np.array_equal(bits(Y), expected_bits(ref, dtype)), f"scatter {policy}"
     # partials + the fold with bias
     Yp = torch.empty((P, M, N), dtype=torch.float32, device=DEV)
     tl.tp_linear_row(Xd, Wd, Yp, P, tl.TP_ROW_PARTIAL)
@@ -158,8 +161,10 @@ def test_row_bias_fused_equals_sum_random(P):
     Yf = torch.empty_like(Ys)
     tl.tp_linear_row_ex(Xd, Wd, Ys, P, tl.TP_ROW_SUM, workspace(tl.TP_ROW_SUM, M, N, P), bias=bd)
     ws = workspace(tl.TP_ROW_FUSED, M, N, P)
-    tl.tp_linear_row_ex(Xd, Wd, Yf, P, tl.TP_ROW_FUSED, ws, bias=bd)
-    assert torch.equal(Ys.view(torch.int16), Yf.view(torch.int16))
+    for policy in FOLD_POLICIES:
+        with row_fold(policy):
+            tl.tp_linear_row_ex(Xd, Wd, Yf, P, tl.TP_ROW_FUSED, ws, bias=bd)
+        assert torch.equal(Ys.view(torch.int16), Yf.view(torch.int16)), policy
     # partials, then the fold with the bias: the same bits again
     Yp = torch.empty((P, M, N), dtype=torch.float32, device=DEV)
     tl.tp_linear_row(Xd, Wd, Yp, P, tl.TP_ROW_PARTIAL)

@@ -10,8 +10,10 @@ and an accumulation-order difference would show:
     the TP_Y_SHARDS blocks are the column blocks of TP_Y_CONCAT;
   * row-parallel with P = 1 equals column-parallel with P = 1;
   * TP_ROW_FUSED equals TP_ROW_SUM (the fold inside the GEMM adds the same
-    fp32 partials in the same order), and leaves the workspace untouched on
-    the decode shapes it fuses;
+    fp32 partials in the same order), both where the library picks the way
+    to fold and with every shape a fused kernel takes sent to it
+    (TPLINEAR_ROW_FOLD=gemm), and then leaves the workspace untouched on the
+    decode shapes;
   * TP_ROW_SCATTER slices are the row blocks of TP_ROW_SUM, with and without
     gaps between the slices;
   * nothing outside an output view is written (guard cells keep their bits);
@@ -23,7 +25,7 @@ import torch
 
 import synth
 import tensor_linear_amd as tl
-from gpu_util import DEV, bf16_dev, f32_dev, bits, workspace
+from gpu_util import DEV, FOLD_POLICIES, bf16_dev, f32_dev, bits, row_fold, workspace
 
 pytestmark = pytest.mark.gpu
 
@@ -147,19 +149,23 @@ def test_fused_equals_sum(shape):
         if K % p:
             continue
         s = bits(_row_y(X, W, p, tl.TP_ROW_SUM, dt, M, N))
-        f = bits(_row_y(X, W, p, tl.TP_ROW_FUSED, dt, M, N))
-        assert np.array_equal(s, f), f"P={p}"
+        for policy in FOLD_POLICIES:
+            with row_fold(policy):
+                f = bits(_row_y(X, W, p, tl.TP_ROW_FUSED, dt, M, N))
+            assert np.array_equal(s, f), f"P={p} {policy}"
 
 
 @pytest.mark.parametrize("M,K,N,P", [(1, 2048, 1000, 8), (16, 4160, 1000, 8),
                                      (64, 1536, 264, 3)])
 def test_fused_decode_leaves_workspace(M, K, N, P):
-    """The fused decode path needs no partials in memory."""
+    """The fused decode path needs no partials in memory (sent to it at
+    every decode shape)."""
     X, W = _inputs(M, K, N, "bf16", 940)
     nbytes = tl.tp_row_workspace_bytes(tl.TP_ROW_FUSED, M, N, P)
     ws = torch.full((nbytes // 4,), NAN32, dtype=torch.int32, device=DEV)
     Y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
-    tl.tp_linear_row(X, W, Y, P, tl.TP_ROW_FUSED, ws.view(torch.uint8))
+    with row_fold("gemm"):
+        tl.tp_linear_row(X, W, Y, P, tl.TP_ROW_FUSED, ws.view(torch.uint8))
     torch.cuda.synchronize()
     assert bool((ws == NAN32).all()), "workspace written"
     assert not torch.isnan(Y.float()).any()

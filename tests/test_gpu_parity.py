@@ -17,7 +17,8 @@ import torch
 import oracle
 import synth
 import tensor_linear_amd as tl
-from gpu_util import DEV, bf16_dev, f32_dev, to_f64, bits, expected_bits, workspace, bf16_tol
+from gpu_util import (DEV, FOLD_POLICIES, bf16_dev, f32_dev, to_f64, bits, expected_bits, row_fold,
+                      workspace, bf16_tol)
 
 pytestmark = pytest.mark.gpu
 
@@ -56,18 +57,21 @@ def _run_all_modes(Xd, Wd, X64, Wio, M, K, N, P, dtype):
     for i, pi in enumerate(oracle.row_partials(X64, Wio, P)):
         assert np.array_equal(bits(Yp[i]), expected_bits(pi, torch.float32)), f"row partial {i}"
     ref = oracle.row_parallel_linear(X64, Wio, P)
-    for mode in (tl.TP_ROW_SUM, tl.TP_ROW_FUSED):
-        Y = torch.full((M, N), float("nan"), dtype=dtype, device=DEV)
-        tl.tp_linear_row(Xd, Wd, Y, P, mode, workspace(mode, M, N, P))
-        assert np.array_equal(bits(Y), expected_bits(ref, dtype)), f"row mode {mode}"
-    if M % P == 0:
-        Y = torch.full((M, N), float("nan"), dtype=dtype, device=DEV)
-        tl.tp_linear_row(Xd, Wd, Y, P, tl.TP_ROW_SCATTER, workspace(tl.TP_ROW_SCATTER, M, N, P))
-        slices = oracle.reduce_scatter_rows(oracle.row_partials(X64, Wio, P), P)
-        s = M // P
-        for j, sl in enumerate(slices):
-            assert np.array_equal(bits(Y[j * s:(j + 1) * s]), expected_bits(sl, dtype)), \
-                f"scatter slice {j}"
+    slices = oracle.reduce_scatter_rows(oracle.row_partials(X64, Wio, P), P) if M % P == 0 else None
+    for policy in FOLD_POLICIES:
+        with row_fold(policy):
+            for mode in (tl.TP_ROW_SUM, tl.TP_ROW_FUSED):
+                Y = torch.full((M, N), float("nan"), dtype=dtype, device=DEV)
+                tl.tp_linear_row(Xd, Wd, Y, P, mode, workspace(mode, M, N, P))
+                assert np.array_equal(bits(Y), expected_bits(ref, dtype)), f"row mode {mode} {policy}"
+            if slices is None:
+                continue
+            Y = torch.full((M, N), float("nan"), dtype=dtype, device=DEV)
+            tl.tp_linear_row(Xd, Wd, Y, P, tl.TP_ROW_SCATTER, workspace(tl.TP_ROW_SCATTER, M, N, P))
+            s = M // P
+            for j, sl in enumerate(slices):
+                assert np.array_equal(bits(Y[j * s:(j + 1) * s]), expected_bits(sl, dtype)), \
+                    f"scatter slice {j} {policy}"
 
 
 # Tiny shapes (generic kernel): M in {1,2,3,5}, P in {1,2,3,4,8},

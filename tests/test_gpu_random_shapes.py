@@ -6,14 +6,15 @@ fold-in-registers and generic kernels with ragged M and N and one to four K
 steps per shard, in bf16 and fp32.  On N(0,1) x N(0, 0.02^2) data, where
 rounding happens in every sum, the fused fold and the one-call
 reduce-scatter must still equal partials + fold bit for bit (the same fp32
-operations in the same order)."""
+operations in the same order), both where the library picks the way to fold
+and with every shape a fused kernel takes sent to it."""
 import numpy as np
 import pytest
 import torch
 
 import synth
 import tensor_linear_amd as tl
-from gpu_util import DEV, bf16_dev, bits, f32_dev, workspace
+from gpu_util import DEV, FOLD_POLICIES, bf16_dev, bits, f32_dev, row_fold, workspace
 from test_gpu_parity import _run_all_modes
 
 pytestmark = pytest.mark.gpu
@@ -54,11 +55,13 @@ def test_random_shapes_fused_equals_sum(case):
     print(f"case M={M} K={K} N={N} P={P} seed={seed}", flush=True)
     X = bf16_dev(synth.to_bf16_bits(synth.normal_f32(seed, (M, K))))
     W = bf16_dev(synth.to_bf16_bits(synth.normal_f32(seed + 1, (N, K), 0.02)))
-    ys = {}
-    modes = [tl.TP_ROW_SUM, tl.TP_ROW_FUSED] + ([tl.TP_ROW_SCATTER] if M % P == 0 else [])
-    for mode in modes:
-        Y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
-        tl.tp_linear_row(X, W, Y, P, mode, workspace(mode, M, N, P))
-        ys[mode] = bits(Y)
-    for mode in modes[1:]:
-        assert np.array_equal(ys[mode], ys[tl.TP_ROW_SUM]), f"mode {mode}"
+    Y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    tl.tp_linear_row(X, W, Y, P, tl.TP_ROW_SUM, workspace(tl.TP_ROW_SUM, M, N, P))
+    ref = bits(Y)
+    modes = [tl.TP_ROW_FUSED] + ([tl.TP_ROW_SCATTER] if M % P == 0 else [])
+    for policy in FOLD_POLICIES:
+        with row_fold(policy):
+            for mode in modes:
+                Y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+                tl.tp_linear_row(X, W, Y, P, mode, workspace(mode, M, N, P))
+                assert np.array_equal(bits(Y), ref), f"mode {mode} {policy}"

@@ -2,7 +2,9 @@
 shapes): bitwise equal to the unfused sequence (fp32 partials + ascending
 fold, TP_ROW_SUM) on N(0,1) x N(0, 0.02^2) data at the workload shapes with
 reduced M, with and without the row bias, ragged M and N tiles, P = 1, and
-against the oracle on sampled rows."""
+against the oracle on sampled rows.  These shapes have fewer tiles than the
+library takes the fold in registers for by itself, so every test here runs
+with TPLINEAR_ROW_FOLD=gemm, which sends every shape the kernel takes to it."""
 import numpy as np
 import pytest
 import torch
@@ -10,9 +12,15 @@ import torch
 import oracle
 import synth
 import tensor_linear_amd as tl
-from gpu_util import DEV, bits, to_f64, workspace, bf16_tol
+from gpu_util import DEV, bits, to_f64, workspace, bf16_tol, row_fold
 
 pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _fold_in_gemm():
+    with row_fold("gemm"):
+        yield
 
 SHAPES = [
     # (M, K, N, P, bias)

@@ -55,6 +55,25 @@ def test_launch_offsets_follow_layout(tmp_path):
     assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr
 
 
+@pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not found")
+def test_row_fold_routing(tmp_path):
+    """Which way TP_ROW_FUSED / TP_ROW_SCATTER fold (inside the GEMM or
+    partials + fold, the same bits either way) for a GPU of 256 CUs, with
+    the library's own choice, TPLINEAR_ROW_FOLD=gemm, and a workspace the
+    partials would not fit (tests/host/route_driver.cpp)."""
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROOT, "tensor_linear_amd", "csrc"),
+           "-I", "/opt/rocm/include", "-D__HIP_PLATFORM_AMD__"]
+    obj = str(tmp_path / "tplinear.o")
+    _run(["g++", "-std=c++17", "-O1", "-c", os.path.join(ROOT, "tensor_linear_amd", "csrc", "tplinear.cpp"),
+          "-o", obj] + SAN + inc, tmp_path)
+    exe = str(tmp_path / "route_driver")
+    _run(["g++", "-std=c++17", "-O1", os.path.join(HOST, "route_driver.cpp"), obj, "-o", exe] + SAN + inc,
+         tmp_path)
+    r = _run([exe], tmp_path)
+    assert "route driver ok" in r.stdout
+    assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr
+
+
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not found")
 def test_oracle_under_sanitizers(tmp_path):
     exe = str(tmp_path / "oracle_driver")
