@@ -1,4 +1,4 @@
-// Skinny shard GEMM for decode-shaped inputs (M <= 64 tokens): C_i = A_i B_i^T
+// Skinny shard GEMM for decode-shaped inputs (M <= 48 tokens): C_i = A_i B_i^T
 // where the weight dominates the bytes, so the kernel is bound by how fast
 // it streams W from HBM ("模型并行", "Tensor Parallel": Y_i = X W_i for the
 // column form, the partials X_i W_i for the row form).
@@ -343,8 +343,12 @@ hipError_t launch_gemm_skinny(const GemmArgs &g, int out_type, const FoldArgs *f
         return launch_mb<2, 2, 256, 2>(g, out_type, fold, ex, s);             // 80 KB
     }
     if (fold) return launch_mb<2, 4, 128, 3>(g, out_type, fold, ex, s);       // 104 KB
-    if (g.M <= 48) return launch_mb<4, 3, 256, 2>(g, out_type, fold, ex, s);  // 160 KB
-    return launch_mb<4, 4, 128, 2>(g, out_type, fold, ex, s);                 // 128 KB
+    // Above 48 tokens the tile kernels' order of work is faster (same box, 8
+    // shards, us after a read-only flush / warm, 64 tokens, skinny vs 128 x
+    // 128 tiles: column 4096 -> 28672 79.8 / 75.1 vs 59.3 / 39.0, 8192 ->
+    // 28672 146.1 / 146.9 vs 106.0 / 106.3; row partials + fold 14336 ->
+    // 4096 50.7 / 45.8 vs 31.9 / 27.1), so no call reaches here with more.
+    return launch_mb<4, 3, 256, 2>(g, out_type, fold, ex, s);                 // 160 KB
 }
 
 }  // namespace tpl

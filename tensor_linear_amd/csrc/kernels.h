@@ -72,7 +72,7 @@ bool gemm_tile_supported(const GemmArgs &g, const GemmExtra *ex);
 hipError_t launch_gemm_narrow(const GemmArgs &g, int out_type, const GemmExtra *ex,
                               hipStream_t s);
 
-// Skinny (M <= 64) bf16 kernel that streams W.  Requires K > 0, K % 8 == 0,
+// Skinny (M <= 48) bf16 kernel that streams W.  Requires K > 0, K % 8 == 0,
 // lda, ldb, a_shard, b_shard multiples of 8 and A, B 16-byte aligned.
 // fold == nullptr: C_i written as out_type.  fold != nullptr: C is unused
 // and the fold of the P shard products is written to fold->Y.
@@ -81,7 +81,7 @@ hipError_t launch_gemm_narrow(const GemmArgs &g, int out_type, const GemmExtra *
 hipError_t launch_gemm_skinny(const GemmArgs &g, int out_type, const FoldArgs *fold,
                               const GemmExtra *ex, hipStream_t s);
 bool gemm_skinny_supported(const GemmArgs &g, const GemmExtra *ex);
-constexpr int SKINNY_MAX_M = 64;
+constexpr int SKINNY_MAX_M = 48;
 
 // Any shape, stride or alignment; fp32 or bf16 inputs; every GemmExtra option.
 hipError_t launch_gemm_generic(const GemmArgs &g, int in_type, int out_type,

@@ -70,7 +70,7 @@ int64_t view_stride(int64_t rows, int64_t cols, int64_t ld, int32_t kind, int32_
 }
 
 // Run one grouped shard GEMM with the best kernel that takes it.
-// Decode-shaped bf16 problems (M <= 64) stream W with the skinny kernel;
+// Decode-shaped bf16 problems (M <= 48) stream W with the skinny kernel;
 // aligned bf16 problems use the 256x256 MFMA tile kernel, or its narrow
 // forms (128x128, or 256x128 with two waves per SIMD) when the 256x256
 // tiles would fill at most half of the CUs; everything else (fp32, odd K,
@@ -287,10 +287,10 @@ bool row_fold_in_gemm_forced() {
 // The two ways to fold give the same bits, so the choice is by speed alone.
 // Same-box times, 8 shards, bf16, us after a read-only 1 GiB flush (warm in
 // brackets), partials + fold vs the fold inside the GEMM:
-// Decode (M <= 64, the skinny kernel): above 16 tokens the fused form loses
-// everywhere (M = 32: 4096 x 14336 -> 4096 33.5 vs 83.1, 8192 -> 8192 38.2 vs
-// 51.8, 28672 -> 8192 100.2 vs 179.7; M = 64: 51.4 vs 92.7, 58.9 vs 60.1,
-// 155.3 vs 175.8).  Up to 16 tokens it wins where its grid fills the CUs
+// Decode (M <= 48, the skinny kernel): above 16 tokens the fused form loses
+// everywhere (M = 32: 14336 -> 4096 33.5 vs 83.1, 8192 -> 8192 38.2 vs 51.8,
+// 28672 -> 8192 100.2 vs 179.7; M = 48: 41.9 vs 93.1, 49.6 vs 59.7, 122.7
+// vs 177.7).  Up to 16 tokens it wins where its grid fills the CUs
 // with 32 output columns per workgroup and the shard's K is long (28672 ->
 // 8192, M = 16: 91.3 vs 95.5; 57344 -> 8192: 155.8 vs 178.3), or where 16
 // columns per workgroup fill them and the layer is small (4096 -> 4096:
@@ -312,7 +312,7 @@ bool skinny_fold_faster(int64_t M, int64_t N, int64_t Ks) {
 // 256 201.7 vs 242.0; K/P = 2048, 16384 -> 8192: 192 241.3 vs 212.1, 256
 // 228.9 vs 282.3.  So: tiles >= CUs * min(1, (K/P + 512) / 2048).
 bool rowfold_faster(int64_t M, int64_t N, int64_t Ks) {
-    if (M <= 64) return false;
+    if (M <= 64) return false;   // its 256-row tile would be three-quarters empty
     const int64_t tiles = ((M + 255) / 256) * ((N + 127) / 128);
     return tiles * 2048 >= (int64_t)device_cu_count() * std::min<int64_t>(2048, Ks + 512);
 }

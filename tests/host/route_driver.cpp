@@ -19,7 +19,7 @@
 namespace tpl {
 // The shapes the fused kernels take (the real checks also look at alignment
 // and leading dims, which every call below satisfies).
-bool gemm_skinny_supported(const GemmArgs &g, const GemmExtra *) { return g.M >= 1 && g.M <= 64; }
+bool gemm_skinny_supported(const GemmArgs &g, const GemmExtra *) { return g.M >= 1 && g.M <= 48; }
 bool gemm_rowfold_supported(const GemmArgs &g, const ReduceArgs &r) {
     return g.K % 64 == 0 && !(r.slice_rows < g.M && r.slice_rows % 256 != 0);
 }
@@ -84,8 +84,10 @@ int main() {
     EXPECT(TP_ROW_FUSED, 16, 4096, 1088, 8, PF);
     EXPECT(TP_ROW_FUSED, 16, 4096, 1792, 8, PF);
     EXPECT(TP_ROW_FUSED, 17, 8192, 3584, 8, PF);   // above 16 tokens: partials + fold
-    EXPECT(TP_ROW_FUSED, 64, 4096, 512, 8, PF);
+    EXPECT(TP_ROW_FUSED, 48, 4096, 512, 8, PF);
+    EXPECT(TP_ROW_FUSED, 64, 4096, 512, 8, PF);    // past the skinny kernel's 48 tokens
     EXPECT(TP_ROW_FUSED, 16, 65536, 1024, 8, PF);  // never the 256-row kernel for M <= 64
+    EXPECT(TP_ROW_FUSED, 64, 65536, 1024, 8, PF);
     // Prefill: tiles = ceil(M / 256) * ceil(N / 128) against 256 * min(1, (K/P + 512) / 2048).
     EXPECT(TP_ROW_FUSED, 4096, 4096, 1792, 8, RF);   // 512 tiles
     EXPECT(TP_ROW_FUSED, 2048, 4096, 1792, 8, RF);   // 256
@@ -111,14 +113,16 @@ int main() {
     EXPECT(TP_ROW_SCATTER, 16, 8192, 3584, 8, PF);     // the decode kernel has no scatter form
     // Partials that would not fit the caller's workspace: every shape a
     // fused kernel takes folds inside the GEMM.
-    EXPECT(TP_ROW_FUSED, 64, 32768, 64, 8, SK, (size_t)32 << 20);
+    EXPECT(TP_ROW_FUSED, 48, 32768, 64, 8, SK, (size_t)32 << 20);
+    EXPECT(TP_ROW_FUSED, 64, 32768, 64, 8, RF, (size_t)32 << 20);
     EXPECT(TP_ROW_FUSED, 2048, 1024, 1024, 8, RF, (size_t)32 << 20);
     EXPECT(TP_ROW_FUSED, 2048, 1024, 1024, 8, PF, (size_t)64 << 20);   // they fit
     EXPECT(TP_ROW_FUSED, 4096, 4096, 8192, 8, PF, (size_t)32 << 20);   // no kernel takes it
     EXPECT(TP_ROW_SUM, 2048, 1024, 1024, 8, PF, (size_t)32 << 20);     // TP_ROW_SUM never folds inside
     // TPLINEAR_ROW_FOLD=gemm: the same, whatever the sizes.
     setenv("TPLINEAR_ROW_FOLD", "gemm", 1);
-    EXPECT(TP_ROW_FUSED, 64, 4096, 512, 8, SK);
+    EXPECT(TP_ROW_FUSED, 48, 4096, 512, 8, SK);
+    EXPECT(TP_ROW_FUSED, 64, 4096, 512, 8, RF);
     EXPECT(TP_ROW_FUSED, 16, 8192, 1024, 8, SK);
     EXPECT(TP_ROW_FUSED, 65, 4096, 64, 8, RF);
     EXPECT(TP_ROW_FUSED, 1024, 4096, 1792, 8, RF);

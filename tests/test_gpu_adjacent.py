@@ -50,7 +50,7 @@ def _ints(seed, shape, lo=-2, hi=2):
 
 BIAS_COL = [
     (7, 512, 3 * 48, 3, torch.bfloat16),     # skinny
-    (40, 256, 2 * 16, 2, torch.bfloat16),    # skinny, M in (32, 64]
+    (40, 256, 2 * 16, 2, torch.bfloat16),    # skinny, M in (32, 48]
     (300, 128, 2 * 264, 2, torch.bfloat16),  # tile, ragged M and N/P = 264
     (512, 256, 4 * 256, 4, torch.bfloat16),  # tile, whole tiles
     (300, 128, 2 * 260, 2, torch.bfloat16),  # N/P = 260: bias offset not a multiple of 8 -> generic

@@ -30,7 +30,7 @@ from gpu_util import DEV, FOLD_POLICIES, bf16_dev, f32_dev, bits, row_fold, work
 pytestmark = pytest.mark.gpu
 
 # (label, M, K, N, P, dtype): each reaches a different kernel for the column
-# and/or the row GEMM (K/P, M and the tile count decide: skinny for M <= 64,
+# and/or the row GEMM (K/P, M and the tile count decide: skinny for M <= 48,
 # for K/P % 64 == 0 the narrow kernel when the 256 x 256 tiles would fill at
 # most half of the CUs -- 128 x 128 tiles when those fit in one pass, else
 # 256 x 128 -- and the 256 x 256 tile kernel otherwise, the generic kernel
@@ -44,7 +44,8 @@ SHAPES = [
     ("skinny-m1", 1, 2048, 1000, 8, "bf16"),
     ("skinny-m16", 16, 4160, 1000, 8, "bf16"),   # K/P = 520: ragged last stage
     ("skinny-m33", 33, 2048, 4096, 8, "bf16"),
-    ("skinny-m64", 64, 1536, 264, 3, "bf16"),
+    ("skinny-m48", 48, 1536, 264, 3, "bf16"),
+    ("narrow-m64", 64, 1536, 264, 3, "bf16"),
     ("generic-bf16", 130, 576, 520, 8, "bf16"),  # row K/P = 72
     ("generic-f32", 70, 96, 48, 4, "f32"),
 ]
@@ -156,7 +157,7 @@ def test_fused_equals_sum(shape):
 
 
 @pytest.mark.parametrize("M,K,N,P", [(1, 2048, 1000, 8), (16, 4160, 1000, 8),
-                                     (64, 1536, 264, 3)])
+                                     (48, 1536, 264, 3)])
 def test_fused_decode_leaves_workspace(M, K, N, P):
     """The fused decode path needs no partials in memory (sent to it at
     every decode shape)."""

@@ -3,8 +3,8 @@
 X or W is a column view of a buffer whose rows are so far apart that the
 view spans more than 4 GiB.  The tile kernels address a tile's rows with
 32-bit offsets and must not take such views: the launch falls back to the
-generic kernel (M > 64) or takes the decode kernel, whose addresses are
-64-bit (M <= 64).  Every column and row mode is checked bit for bit against
+generic kernel (M > 48) or takes the decode kernel, whose addresses are
+64-bit (M <= 48).  Every column and row mode is checked bit for bit against
 the oracle on integer inputs (all sums exact in fp32), as in the parity suite.
 """
 import numpy as np

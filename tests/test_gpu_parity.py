@@ -89,14 +89,15 @@ def test_brute_force_tiny_bitwise(dt):
         _run_all_modes(Xd, Wd, X64, Wio, M, K, N, P, dtype)
 
 
-# Shapes that reach the skinny (M <= 64), narrow (128 x 128 and 256 x 128)
+# Shapes that reach the skinny (M <= 48), narrow (128 x 128 and 256 x 128)
 # and 256 x 256 tile kernels, with ragged M and N tails; integer inputs keep
 # every sum exact.
 ALIGNED = [
     (16, 8192 // 8 * 8, 256, 8),   # skinny, one m-block
     (1, 512, 64, 8),
     (17, 256, 192, 4),             # skinny, two m-blocks, ragged M
-    (64, 1024, 512, 2),            # skinny, four m-blocks
+    (48, 1024, 512, 2),            # skinny, three m-blocks
+    (64, 1024, 512, 2),            # 128 x 128 tiles, 64 tokens
     (65, 512, 512, 2),             # few tiles: 128 x 128 tiles, mostly-empty M tile
     (300, 512, 2 * 300, 2),        # 128 x 128 tiles, ragged M and N/P = 300
     (512, 1024, 2048, 8),          # 128 x 128 tiles, whole tiles

@@ -119,9 +119,9 @@ def _gemm_inputs(M, KS, N, seed):
             X.astype(np.float64), W.T.astype(np.float64))
 
 
-# (label, M, KS, N): M > 64 and KS % 64 == 0 reach the tile kernel, M <= 64
+# (label, M, KS, N): M > 48 and KS % 64 == 0 reach the tile kernels, M <= 48
 # the skinny kernel (and the fused fold), KS = 72 the generic kernel.
-GEMM_CASES = [("tile", 128, 64, 4096), ("skinny-m64", 64, 64, 4096),
+GEMM_CASES = [("tile", 128, 64, 4096), ("skinny-m48", 48, 64, 4096), ("narrow-m64", 64, 64, 4096),
               ("skinny-m16", 16, 64, 8192), ("generic", 128, 72, 2048)]
 
 

@@ -50,10 +50,10 @@ def test_noalloc_equals_workspace_call(dtype, mode):
 @pytest.mark.parametrize("M,K,N,P,mode", [
     (2048, 8192, 1024, 8, tl.TP_ROW_FUSED),     # prefill, the fold in registers
     (2048, 8192, 1024, 8, tl.TP_ROW_SCATTER),   # the same, into 256-row token slices
-    (64, 512, 32768, 8, tl.TP_ROW_FUSED),       # decode, the fused skinny fold
+    (48, 512, 32768, 8, tl.TP_ROW_FUSED),       # decode, the fused skinny fold
 ])
 def test_noalloc_fused_paths_need_no_workspace(M, K, N, P, mode):
-    # 64 MiB of fp32 partials would not fit the array, but these calls fold
+    # 48 or 64 MiB of fp32 partials would not fit the array, but these calls fold
     # inside the GEMM and use none of it
     print(f"noalloc fused M={M} K={K} N={N} P={P} mode={mode}", flush=True)
     assert tl.tp_row_workspace_bytes(mode, M, N, P) > tl.TP_NOALLOC_SCRATCH_BYTES
