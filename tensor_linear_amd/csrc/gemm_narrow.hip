@@ -3,24 +3,28 @@
 // "Tensor Parallel": the per-shard products Y_i = X W_i and X_i W_i).  Each
 // wave owns a 64 x 64 block of 4 x 4 v_mfma_f32_16x16x32_bf16 blocks, with
 // the instruction and the K order of the 256 x 256 tile kernel, so every
-// output is bitwise the same.  Two tile heights:
+// output is bitwise the same.  Three tile shapes:
 //  - 128 x 128 tiles, four waves in a 2 x 2 grid, when they fit in one pass
 //    over the CUs (up to 128 tokens, and up to 256 when the N side is short):
 //    no MFMA work on rows past M, twice the workgroups of 256-row tiles
 //    where M > 128;
+//  - 128 x 64 tiles where 128 x 128 ones would fill at most half of the CUs:
+//    each wave a 64 x 32 block (4 x 2 MFMA blocks), twice the workgroups
+//    again;
 //  - else 256 x 128 tiles, eight waves in a 4 x 2 grid, two per SIMD: the
 //    second wave on each SIMD issues its MFMAs while the first waits on its
 //    LDS reads and loads.
 //
 // Pipeline (the fold-in-registers kernel's eight-wave form, without the
 // fold): three stages of 64 K columns for both operands (3 x (32 + 16) KB,
-// or 3 x (16 + 16) KB for 128 rows), 128-byte LDS rows with 16-byte chunk c
+// 3 x (16 + 16) KB or 3 x (16 + 8) KB), 128-byte LDS rows with 16-byte chunk c
 // of row r at slot c ^ ((r / 2) % 8), global -> LDS with
-// global_load_lds_dwordx4.  Per K step each wave issues 32 MFMAs in two
-// substeps of 32 K: during substep 0 it reads its substep-1 fragments and
-// issues all of step it+2's loads (6 per wave with 256 rows, 8 with 128)
-// into the stage step it-1 freed; then the step's one barrier; during
-// substep 1 it reads the next step's substep-0 fragments.  Persistent
+// global_load_lds_dwordx4.  Per K step each wave issues 32 MFMAs (16 with
+// 64 columns) in two substeps of 32 K: during substep 0 it reads its
+// substep-1 fragments and issues all of step it+2's loads (6 per wave with
+// 256 rows, 8 with 128, 6 with 64 columns) into the stage step it-1 freed;
+// then the step's one barrier; during substep 1 it reads the next step's
+// substep-0 fragments.  Persistent
 // workgroups walk an XCD-contiguous range of (shard, tile) pairs; the K
 // pipeline runs across tiles.
 #include "kernels.h"
@@ -33,7 +37,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_PTR(T) __attribute__((address_space(3))) T *
 
-constexpr int FN = 128;   // tile columns (output features)
 constexpr int FBK = 64;   // K columns per stage
 constexpr int FGROUP = 4; // tile rows visited as a group
 
@@ -72,15 +75,20 @@ __device__ __forceinline__ int narrow_tile_of(const NarrowSched &ts, int q) {
 }
 
 // FM: tile rows, 256 (eight waves, two per SIMD) or 128 (four waves).
-template <int OUT, int FM>
+// TN: tile columns, 128 or (with 128 rows) 64.
+template <int OUT, int FM, int TN>
 __global__ __attribute__((amdgpu_flat_work_group_size(FM * 2, FM * 2),
                           amdgpu_waves_per_eu(FM / 128, FM / 128)))
 void gemm_narrow_kernel(GemmArgs g, NarrowSched ts, const __bf16 *bias_all, int64_t bias_shard,
                         int vec_store) {
+    static_assert(TN == 128 || (TN == 64 && FM == 128), "tile shapes");
     constexpr int NW = FM / 32;            // waves
+    constexpr int WI = TN / 32;            // 16-column W blocks per wave
+    constexpr int NF = WI + 4;             // fragments per substep
+    constexpr int NU = 4 * WI;             // MFMAs per substep
     constexpr int ROWB = FBK * 2;          // 128 bytes per LDS row
     constexpr int OPX = FM * ROWB;         // X stage, 32 or 16 KB
-    constexpr int OPW = FN * ROWB;         // W stage, 16 KB
+    constexpr int OPW = TN * ROWB;         // W stage, 16 or 8 KB
     constexpr int W_BASE = 3 * OPX;        // three X stages, then three W stages
     constexpr int LX = OPX / 1024 / NW;    // X loads per wave per step (4)
     constexpr int LW = OPW / 1024 / NW;    // W loads per wave per step (2 or 4)
@@ -110,9 +118,9 @@ void gemm_narrow_kernel(GemmArgs g, NarrowSched ts, const __bf16 *bias_all, int6
         int tm, tn;
         narrow_decode(ts, narrow_tile_of(ts, q), psh, tm, tn);
         pm0 = (int64_t)tm * FM;
-        pn0 = (int64_t)tn * FN;
+        pn0 = (int64_t)tn * TN;
         const int a_rows = (int)min<int64_t>(g.M - pm0, FM);
-        const int b_rows = (int)min<int64_t>(g.N - pn0, FN);
+        const int b_rows = (int)min<int64_t>(g.N - pn0, TN);
 #pragma unroll
         for (int j = 0; j < LX; ++j) {
             const int r = (j * NW + wave) * 8 + lane / 8;
@@ -179,23 +187,23 @@ void gemm_narrow_kernel(GemmArgs g, NarrowSched ts, const __bf16 *bias_all, int6
     const int frow = lane & 15;
     const int fq = lane >> 4;
     const int fx = (frow / 2) % 8;
-    const uint32_t wrow_off = (wn * 64 + frow) * ROWB;
+    const uint32_t wrow_off = (wn * (TN / 2) + frow) * ROWB;
     const uint32_t xrow_off = (wm * 64 + frow) * ROWB;
     auto frag_addr = [&](int stage, int f, int h) -> uint32_t {
         const uint32_t slot = (uint32_t)(((4 * h + fq) ^ fx) << 4);
-        if (f < 4) return W_BASE + stage * OPW + wrow_off + f * 16 * ROWB + slot;
-        return stage * OPX + xrow_off + (f - 4) * 16 * ROWB + slot;
+        if (f < WI) return W_BASE + stage * OPW + wrow_off + f * 16 * ROWB + slot;
+        return stage * OPX + xrow_off + (f - WI) * 16 * ROWB + slot;
     };
-    bf16x8 fr[2][8];
+    bf16x8 fr[2][NF];
     auto read_frag = [&](int h, int f, uint32_t addr) __attribute__((always_inline)) {
         fr[h][f] = *(LDS_PTR(bf16x8))(lds + addr);
     };
 #pragma unroll
-    for (int f = 0; f < 8; ++f) read_frag(0, f, frag_addr(0, f, 0));
+    for (int f = 0; f < NF; ++f) read_frag(0, f, frag_addr(0, f, 0));
 
     int s0 = 0;                 // stage of the current step (step index % 3)
     bool drained = true;        // no epilogue store is in flight
-    f32x4 acc[4][4];
+    f32x4 acc[WI][4];
     for (int q = 0; q < ntiles; ++q) {
         {
             auto kstep = [&](auto first) __attribute__((always_inline)) {
@@ -204,18 +212,21 @@ void gemm_narrow_kernel(GemmArgs g, NarrowSched ts, const __bf16 *bias_all, int6
                 const int s2 = s1 == 2 ? 0 : s1 + 1;   // stage of step it+2 (= it-1's)
                 // substep 0: the substep-1 fragments, step it+2's loads
 #pragma unroll
-                for (int u = 0; u < 16; ++u) {
+                for (int u = 0; u < NU; ++u) {
                     __builtin_amdgcn_sched_barrier(0);
-                    const int i = u & 3, j = u >> 2;
+                    const int i = u % WI, j = u / WI;
                     if (FIRST)   // the shard's first product of each block: C = 0
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[0][i], fr[0][4 + j], f32x4{}, 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[0][i], fr[0][WI + j], f32x4{}, 0, 0, 0);
                     else
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[0][i], fr[0][4 + j], acc[i][j], 0, 0, 0);
-                    const bool rd = (u & 1) == 0;
-                    if (rd) read_frag(1, u >> 1, frag_addr(s0, u >> 1, 1));
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[0][i], fr[0][WI + j], acc[i][j], 0, 0, 0);
+                    const bool rd = NU >= 2 * NF ? (u & 1) == 0 : u < NF;
+                    const int ri = NU >= 2 * NF ? u >> 1 : u;
+                    if (rd) read_frag(1, ri, frag_addr(s0, ri, 1));
                     // step it+2's loads, X then W: six at MFMAs 1, 3, 6, 9,
-                    // 11, 14 (256 rows) or eight at the odd MFMAs (128 rows)
-                    const int li = LX + LW == 8 ? ((u & 1) ? (u >> 1) : -1)
+                    // 11, 14 (256 rows), eight at the odd MFMAs (128 rows)
+                    // or six at MFMAs 1-6 (64 columns)
+                    const int li = NU == 8 ? (u >= 1 && u <= LX + LW ? u - 1 : -1)
+                                 : LX + LW == 8 ? ((u & 1) ? (u >> 1) : -1)
                                  : u == 1 ? 0 : u == 3 ? 1 : u == 6 ? 2 : u == 9 ? 3 : u == 11 ? 4 : u == 14 ? 5 : -1;
                     if (li >= 0) load(s2, li);
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
@@ -238,12 +249,13 @@ void gemm_narrow_kernel(GemmArgs g, NarrowSched ts, const __bf16 *bias_all, int6
                 // substep 1: the next step's substep-0 fragments (W0-3, then
                 // X0-3, the order its first MFMAs use them)
 #pragma unroll
-                for (int u = 0; u < 16; ++u) {
+                for (int u = 0; u < NU; ++u) {
                     __builtin_amdgcn_sched_barrier(0);
-                    const int i = u & 3, j = u >> 2;
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[1][i], fr[1][4 + j], acc[i][j], 0, 0, 0);
-                    const bool rd = (u & 1) == 0;
-                    if (rd) read_frag(0, u >> 1, frag_addr(s1, u >> 1, 0));
+                    const int i = u % WI, j = u / WI;
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[1][i], fr[1][WI + j], acc[i][j], 0, 0, 0);
+                    const bool rd = NU >= 2 * NF ? (u & 1) == 0 : u < NF;
+                    const int ri = NU >= 2 * NF ? u >> 1 : u;
+                    if (rd) read_frag(0, ri, frag_addr(s1, ri, 0));
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
                     if (rd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
                 }
@@ -257,13 +269,14 @@ void gemm_narrow_kernel(GemmArgs g, NarrowSched ts, const __bf16 *bias_all, int6
 
         // ---- epilogue: acc (+ bias) -> the output type.  acc[i][j][r] =
         // C[m = 16j + lane%16][n = 16i + 4*(lane/16) + r] of the wave's block.
-        // 16 rows x 64 columns at a time go through this wave's 1 KB chunks
+        // 16 rows x 64 (or 32) columns at a time go through this wave's 1 KB chunks
         // w + NW*c (c = 0..3) of the X stage of the tile's last step (read by
         // everyone before that step's barrier; only this wave's own later
         // loads write these chunks): staging row r of 256 bytes at chunk r/4,
         // offset (r%4)*256, 16-byte slot s at s ^ (r % 16).  Then each lane
         // holds 8 consecutive bf16 outputs of a row (a 64-column row leaves as
-        // one 128-byte line) or 4 consecutive fp32 ones (two lines).
+        // one 128-byte line, a 32-column one as half of one) or 4
+        // consecutive fp32 ones (two lines, or one).
         __builtin_amdgcn_sched_barrier(0);
         int shard, tm, tn;
         narrow_decode(ts, narrow_tile_of(ts, q), shard, tm, tn);
@@ -272,10 +285,12 @@ void gemm_narrow_kernel(GemmArgs g, NarrowSched ts, const __bf16 *bias_all, int6
         auto st_addr = [&](int r, int s) -> LDS_PTR(char) {
             return ep + (r >> 2) * (NW * 1024) + (r & 3) * 256 + ((s ^ (r & 15)) << 4);
         };
-        const int64_t m_t = (int64_t)tm * FM, tm_w = m_t + wm * 64, tn_w = (int64_t)tn * FN + wn * 64;
+        const int64_t m_t = (int64_t)tm * FM, tm_w = m_t + wm * 64, tn_w = (int64_t)tn * TN + wn * (TN / 2);
         const int64_t cbase = (int64_t)shard * g.c_shard;
         const __bf16 *bias = bias_all ? bias_all + (int64_t)shard * bias_shard : nullptr;
-        const int c8 = lane & 7;
+        constexpr int LPR8 = 2 * WI;            // lanes per staged row, 8 bf16 each
+        constexpr int RPP8 = 64 / LPR8;         // rows per pass
+        const int c8 = lane % LPR8;
         const int64_t ncol = tn_w + c8 * 8;
         float bv[8];
 #pragma unroll
@@ -284,16 +299,18 @@ void gemm_narrow_kernel(GemmArgs g, NarrowSched ts, const __bf16 *bias_all, int6
         for (int jj = 0; jj < 4; ++jj) {        // rows 16jj.. of the wave
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int bi = 0; bi < 4; ++bi)
+            for (int bi = 0; bi < WI; ++bi)
                 *(LDS_PTR(f32x4))st_addr(frow, bi * 4 + fq) = acc[bi][jj];
             if constexpr (OUT == OUT_F32) {
-                const int c16 = lane & 15;
-                f32x4 a[4];
+                constexpr int LPR4 = 4 * WI;        // lanes per staged row, 4 fp32 each
+                constexpr int RPP4 = 64 / LPR4;     // rows per pass
+                const int c16 = lane % LPR4;
+                f32x4 a[16 / RPP4];
 #pragma unroll
-                for (int p = 0; p < 4; ++p) a[p] = *(LDS_PTR(f32x4))st_addr(p * 4 + (lane >> 4), c16);
+                for (int p = 0; p < 16 / RPP4; ++p) a[p] = *(LDS_PTR(f32x4))st_addr(p * RPP4 + lane / LPR4, c16);
 #pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const int64_t m = tm_w + jj * 16 + p * 4 + (lane >> 4), n = tn_w + c16 * 4;
+                for (int p = 0; p < 16 / RPP4; ++p) {
+                    const int64_t m = tm_w + jj * 16 + p * RPP4 + lane / LPR4, n = tn_w + c16 * 4;
                     if (m >= g.M) continue;
                     float *dst = (float *)g.C + cbase + m * g.ldc + n;
                     if (vec_store && n + 4 <= g.N) {
@@ -306,16 +323,16 @@ void gemm_narrow_kernel(GemmArgs g, NarrowSched ts, const __bf16 *bias_all, int6
                 }
                 continue;
             }
-            f32x4 a0[2], a1[2];
+            f32x4 a0[16 / RPP8], a1[16 / RPP8];
 #pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                const int rr = p * 8 + (lane >> 3);
+            for (int p = 0; p < 16 / RPP8; ++p) {
+                const int rr = p * RPP8 + lane / LPR8;
                 a0[p] = *(LDS_PTR(f32x4))st_addr(rr, 2 * c8);
                 a1[p] = *(LDS_PTR(f32x4))st_addr(rr, 2 * c8 + 1);
             }
 #pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                const int rr = p * 8 + (lane >> 3);
+            for (int p = 0; p < 16 / RPP8; ++p) {
+                const int rr = p * RPP8 + lane / LPR8;
                 const int64_t m = tm_w + jj * 16 + rr;
                 if (m >= g.M) continue;
                 float v[8] = {a0[p][0], a0[p][1], a0[p][2], a0[p][3], a1[p][0], a1[p][1], a1[p][2], a1[p][3]};
@@ -357,9 +374,17 @@ hipError_t launch_gemm_narrow(const GemmArgs &g, int out_type, const GemmExtra *
     // M = 256, 8192 -> 10240: 83.9 / 62.0 vs 110.7 / 88.6; M = 200,
     // 4096 -> 14336: 49.0 / 41.6 vs 57.6 / 49.4.  Bitwise equal.
     const int cus = device_cu_count();
-    const int64_t tn = (g.N + FN - 1) / FN;
-    const int FM = ((g.M + 127) / 128) * tn * g.P <= cus ? 128 : 256;
+    const int64_t tn128 = (g.N + 127) / 128;
+    const int FM = ((g.M + 127) / 128) * tn128 * g.P <= cus ? 128 : 256;
     const int64_t tm = (g.M + FM - 1) / FM;
+    // 64-column tiles where 128 x 128 ones would fill at most half of the
+    // CUs.  Same box, 8 shards, us after a read-only 1 GiB flush / warm, 64-
+    // vs 128-column tiles: M = 65, 8192 -> 10240 65.6 / 48.4 vs 74.5 / 55.6;
+    // M = 128 70.1 / 51.6 vs 81.5 / 55.8; M = 128, 4096 -> 4096 36.9 / 27.3
+    // vs 43.3 / 30.9; row partials M = 128, 8192 -> 2048 15.0 / 12.2 vs
+    // 17.7 / 14.4.  Bitwise equal.
+    const int TN = (FM == 128 && 2 * tm * tn128 * g.P <= cus) ? 64 : 128;
+    const int64_t tn = (g.N + TN - 1) / TN;
     const int64_t T = tm * tn * g.P;
     if (T > 0x7FFFFFFFll) return hipErrorInvalidConfiguration;
     NarrowSched ts;
@@ -372,15 +397,20 @@ hipError_t launch_gemm_narrow(const GemmArgs &g, int out_type, const GemmExtra *
     const int vw = out_type == OUT_BF16 ? 8 : 4;
     const int vec = g.ldc % vw == 0 && g.c_shard % vw == 0 && aligned16(g.C);
     const __bf16 *bias = (const __bf16 *)ex.bias;
-    if (FM == 128) {
+    if (TN == 64) {
         if (out_type == OUT_BF16)
-            gemm_narrow_kernel<OUT_BF16, 128><<<dim3(grid), dim3(256), 0, s>>>(g, ts, bias, ex.bias_shard, vec);
+            gemm_narrow_kernel<OUT_BF16, 128, 64><<<dim3(grid), dim3(256), 0, s>>>(g, ts, bias, ex.bias_shard, vec);
         else
-            gemm_narrow_kernel<OUT_F32, 128><<<dim3(grid), dim3(256), 0, s>>>(g, ts, nullptr, 0, vec);
+            gemm_narrow_kernel<OUT_F32, 128, 64><<<dim3(grid), dim3(256), 0, s>>>(g, ts, nullptr, 0, vec);
+    } else if (FM == 128) {
+        if (out_type == OUT_BF16)
+            gemm_narrow_kernel<OUT_BF16, 128, 128><<<dim3(grid), dim3(256), 0, s>>>(g, ts, bias, ex.bias_shard, vec);
+        else
+            gemm_narrow_kernel<OUT_F32, 128, 128><<<dim3(grid), dim3(256), 0, s>>>(g, ts, nullptr, 0, vec);
     } else if (out_type == OUT_BF16) {
-        gemm_narrow_kernel<OUT_BF16, 256><<<dim3(grid), dim3(512), 0, s>>>(g, ts, bias, ex.bias_shard, vec);
+        gemm_narrow_kernel<OUT_BF16, 256, 128><<<dim3(grid), dim3(512), 0, s>>>(g, ts, bias, ex.bias_shard, vec);
     } else {
-        gemm_narrow_kernel<OUT_F32, 256><<<dim3(grid), dim3(512), 0, s>>>(g, ts, nullptr, 0, vec);
+        gemm_narrow_kernel<OUT_F32, 256, 128><<<dim3(grid), dim3(512), 0, s>>>(g, ts, nullptr, 0, vec);
     }
     return hipGetLastError();
 }

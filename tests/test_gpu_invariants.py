@@ -32,12 +32,13 @@ pytestmark = pytest.mark.gpu
 # (label, M, K, N, P, dtype): each reaches a different kernel for the column
 # and/or the row GEMM (K/P, M and the tile count decide: skinny for M <= 48,
 # for K/P % 64 == 0 the narrow kernel when the 256 x 256 tiles would fill at
-# most half of the CUs -- 128 x 128 tiles when those fit in one pass, else
-# 256 x 128 -- and the 256 x 256 tile kernel otherwise, the generic kernel
+# most half of the CUs -- 128 x 128 tiles when those fit in one pass, 128 x 64
+# when they would fill at most half of it, else 256 x 128 -- and the 256 x 256
+# tile kernel otherwise, the generic kernel
 # for other K and for fp32).  Column P shards against P = 1 compares the
 # 256 x 256 tile kernel with the 256 x 128 narrow tiles on "tile-ragged".
 SHAPES = [
-    ("narrow", 300, 1024, 1024, 8, "bf16"),          # few tiles: 128 x 128 tiles
+    ("narrow", 300, 1024, 1024, 8, "bf16"),          # column 128 x 64 tiles, row 128 x 128
     ("narrow-ragged", 257, 512, 520, 4, "bf16"),
     ("narrow256", 520, 1024, 2048, 4, "bf16"),       # row partials of 4 shards: 256 x 128 tiles
     ("tile-ragged", 1100, 1024, 4224, 16, "bf16"),   # 160 / 1360 256 x 256 tiles

@@ -89,22 +89,24 @@ def test_brute_force_tiny_bitwise(dt):
         _run_all_modes(Xd, Wd, X64, Wio, M, K, N, P, dtype)
 
 
-# Shapes that reach the skinny (M <= 48), narrow (128 x 128 and 256 x 128)
-# and 256 x 256 tile kernels, with ragged M and N tails; integer inputs keep
-# every sum exact.
+# Shapes that reach the skinny (M <= 48), narrow (128 x 64, 128 x 128 and
+# 256 x 128) and 256 x 256 tile kernels, with ragged M and N tails; integer
+# inputs keep every sum exact.
 ALIGNED = [
     (16, 8192 // 8 * 8, 256, 8),   # skinny, one m-block
     (1, 512, 64, 8),
     (17, 256, 192, 4),             # skinny, two m-blocks, ragged M
     (48, 1024, 512, 2),            # skinny, three m-blocks
-    (64, 1024, 512, 2),            # 128 x 128 tiles, 64 tokens
-    (65, 512, 512, 2),             # few tiles: 128 x 128 tiles, mostly-empty M tile
-    (300, 512, 2 * 300, 2),        # 128 x 128 tiles, ragged M and N/P = 300
-    (512, 1024, 2048, 8),          # 128 x 128 tiles, whole tiles
-    (256, 64 * 8, 256 * 8, 8),     # 128 x 128 tiles, K/P = 64 (one K step)
-    (200, 512, 260 * 4, 4),        # 128 x 128 tiles, two M tiles, ragged M and N/P = 260
+    (64, 1024, 512, 2),            # 128 x 64 tiles, 64 tokens
+    (65, 512, 512, 2),             # few tiles: 128 x 64 tiles, mostly-empty M tile
+    (300, 512, 2 * 300, 2),        # 128 x 64 tiles, ragged M and N/P = 300
+    (512, 1024, 2048, 8),          # 128 x 64 tiles, whole tiles
+    (256, 64 * 8, 256 * 8, 8),     # 128 x 64 tiles, K/P = 64 (one K step)
+    (200, 512, 260 * 4, 4),        # 128 x 64 tiles, two M tiles, ragged M and N/P = 260
+    (100, 256, 2200 * 8, 8),       # 128 x 128 tiles (144, more than half the CUs), N/P = 2200
+    (130, 512, 1100 * 8, 8),       # 128 x 128 tiles, two M tiles, ragged M and N/P = 1100
     (1024, 64 * 8, 1024 * 8, 8),   # column: 256 x 128 tiles (128-row tiles would not fit one pass)
-    (520, 1024, 2048, 4),          # row partials: 256 x 128 tiles, ragged M; column: 128 x 128
+    (520, 1024, 2048, 4),          # row partials: 256 x 128 tiles, ragged M; column: 128 x 64
     (1100, 1024, 264 * 16, 16),    # 256 x 256 tile kernel (160 tiles), ragged M and N/P = 264
     (40, 24, 42, 3),               # skinny with K/P = 8 (K tail)
     (257, 72 * 2, 130, 2),         # generic (K/P = 72 is not a multiple of 64)
