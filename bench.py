@@ -438,7 +438,8 @@ def platform_reference(wl, steps, torch):
     (torch.nn.functional.linear, hipBLASLt) on each column GEMM's dense
     equivalent -- X [M, K] times all N rows of W, the same flops and the same
     output -- and on the row GEMM's full-K product (the same flops, one bf16
-    output instead of P fp32 partials).  Embedding: F.embedding of the same
+    output instead of P fp32 partials); for decode also the rate of the bytes
+    it must stream (W + X + Y).  Embedding: F.embedding of the same
     batches of ids over the P shard tables concatenated into one [V, D] table
     (the same bytes moved as the library's lookup), and the per-shard gather
     followed by torch.cat (what the same lookup costs written with torch ops
@@ -459,10 +460,12 @@ def platform_reference(wl, steps, torch):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps * 1e3   # us
 
-    if wl.wid in (2, 3, 5, 6, 7):
+    if wl.wid in (2, 3, 4, 5, 6, 7):
         pairs = []
         if wl.wid in (2, 3):
             pairs = [("column_gemm", wl.X1, wl.W1), ("row_gemm_full_k", wl.X2, wl.W2)]
+        elif wl.wid == 4:
+            pairs = [("column_gemm_decode", wl.X1, wl.W1), ("row_gemm_full_k", wl.X2, wl.W2)]
         elif wl.wid in (5, 7):
             pairs = [("row_gemm_full_k", wl.X1, wl.W1), ("column_gemm", wl.Y, wl.W3)]
         elif wl.wid == 6:
@@ -473,6 +476,10 @@ def platform_reference(wl, steps, torch):
             out[name] = dict(avg_us=us, tflops=fl / us / 1e6,
                              frac_bf16_peak=fl / us / 1e6 / PEAK_BF16_TFLOPS,
                              kernel="torch.nn.functional.linear (platform GEMM)")
+            if wl.wid == 4:   # decode: bound by streaming W
+                nbytes = (W.numel() + X.numel() + X.shape[0] * W.shape[0]) * 2
+                out[name].update(algorithmic_bytes=nbytes, gbps=nbytes / us / 1e3,
+                                 frac_hbm_peak=nbytes / us / 1e3 / PEAK_HBM_GBPS)
     elif wl.wid == 8:
         T, D = wl.ids.shape[0], wl.Y1.shape[1]
         nbytes = T * D * 2 * 2 + T * 8
