@@ -14,6 +14,9 @@
 //  - else 256 x 128 tiles, eight waves in a 4 x 2 grid, two per SIMD: the
 //    second wave on each SIMD issues its MFMAs while the first waits on its
 //    LDS reads and loads.
+// Epilogues: bf16 (+ the column bias), fp32 partials, or the gated unit of a
+// fused gate+up layer (128-column W tiles: half gate rows, half the up rows
+// of the same hidden units, the tile kernel's arithmetic).
 //
 // Pipeline (the fold-in-registers kernel's eight-wave form, without the
 // fold): three stages of 64 K columns for both operands (3 x (32 + 16) KB,
@@ -75,13 +78,18 @@ __device__ __forceinline__ int narrow_tile_of(const NarrowSched &ts, int q) {
 }
 
 // FM: tile rows, 256 (eight waves, two per SIMD) or 128 (four waves).
-// TN: tile columns, 128 or (with 128 rows) 64.
-template <int OUT, int FM, int TN>
+// TN: tile columns (W rows), 128 or (with 128 rows) 64.
+// SW: the gated unit of a fused gate+up layer: of each wave's four W blocks
+// two are gate rows and two the up rows (up_off further on) of the same 32
+// hidden units, so a tile gives TN / 2 outputs silu(g + bg) * (u + bu).
+template <int OUT, int FM, int TN, bool SW = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(FM * 2, FM * 2),
                           amdgpu_waves_per_eu(FM / 128, FM / 128)))
 void gemm_narrow_kernel(GemmArgs g, NarrowSched ts, const __bf16 *bias_all, int64_t bias_shard,
-                        int vec_store) {
+                        int vec_store, int64_t up_off) {
     static_assert(TN == 128 || (TN == 64 && FM == 128), "tile shapes");
+    static_assert(!SW || (TN == 128 && OUT == OUT_BF16), "the gated unit: 128 W rows, bf16 out");
+    constexpr int TBN = SW ? TN / 2 : TN;  // output columns per tile
     constexpr int NW = FM / 32;            // waves
     constexpr int WI = TN / 32;            // 16-column W blocks per wave
     constexpr int NF = WI + 4;             // fragments per substep
@@ -118,9 +126,9 @@ void gemm_narrow_kernel(GemmArgs g, NarrowSched ts, const __bf16 *bias_all, int6
         int tm, tn;
         narrow_decode(ts, narrow_tile_of(ts, q), psh, tm, tn);
         pm0 = (int64_t)tm * FM;
-        pn0 = (int64_t)tn * TN;
+        pn0 = (int64_t)tn * TBN;
         const int a_rows = (int)min<int64_t>(g.M - pm0, FM);
-        const int b_rows = (int)min<int64_t>(g.N - pn0, TN);
+        const int b_rows = (int)min<int64_t>(g.N - pn0, TBN);
 #pragma unroll
         for (int j = 0; j < LX; ++j) {
             const int r = (j * NW + wave) * 8 + lane / 8;
@@ -132,8 +140,17 @@ void gemm_narrow_kernel(GemmArgs g, NarrowSched ts, const __bf16 *bias_all, int6
         for (int j = 0; j < LW; ++j) {
             const int r = (j * NW + wave) * 8 + lane / 8;
             const int chunk = (lane % 8) ^ ((r / 2) % 8);
-            const int rb = r < b_rows ? r : b_rows - 1;
-            boff[j] = (uint32_t)(((int64_t)rb * g.ldb + chunk * 8) * 2);
+            int64_t rb;
+            if constexpr (SW) {
+                // LDS row r feeds wave column r / 64, W block (r / 16) % 4:
+                // blocks 0-1 gate rows, 2-3 the up rows of the same 32 units.
+                int h = ((r >> 6) << 5) + (((r >> 4) & 1) << 4) + (r & 15);
+                h = h < b_rows ? h : b_rows - 1;
+                rb = h + (((r >> 4) & 2) ? up_off : 0);
+            } else {
+                rb = r < b_rows ? r : b_rows - 1;
+            }
+            boff[j] = (uint32_t)((rb * g.ldb + chunk * 8) * 2);
         }
     };
     auto set_bases = [&]() {
@@ -285,7 +302,7 @@ void gemm_narrow_kernel(GemmArgs g, NarrowSched ts, const __bf16 *bias_all, int6
         auto st_addr = [&](int r, int s) -> LDS_PTR(char) {
             return ep + (r >> 2) * (NW * 1024) + (r & 3) * 256 + ((s ^ (r & 15)) << 4);
         };
-        const int64_t m_t = (int64_t)tm * FM, tm_w = m_t + wm * 64, tn_w = (int64_t)tn * TN + wn * (TN / 2);
+        const int64_t m_t = (int64_t)tm * FM, tm_w = m_t + wm * 64, tn_w = (int64_t)tn * TBN + wn * (TBN / 2);
         const int64_t cbase = (int64_t)shard * g.c_shard;
         const __bf16 *bias = bias_all ? bias_all + (int64_t)shard * bias_shard : nullptr;
         constexpr int LPR8 = 2 * WI;            // lanes per staged row, 8 bf16 each
@@ -295,12 +312,51 @@ void gemm_narrow_kernel(GemmArgs g, NarrowSched ts, const __bf16 *bias_all, int6
         float bv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) bv[e] = bias && ncol + e < g.N ? (float)bias[ncol + e] : 0.0f;
+        // gated unit: lane takes 8 hidden units from 8 * (lane % 4) of row lane / 4
+        const int64_t nsw = tn_w + (lane & 3) * 8;
+        float bg[8], bu[8];
+        if constexpr (SW) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                bg[e] = bias && nsw + e < g.N ? (float)bias[nsw + e] : 0.0f;
+                bu[e] = bias && nsw + e < g.N ? (float)bias[up_off + nsw + e] : 0.0f;
+            }
+        }
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {        // rows 16jj.. of the wave
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int bi = 0; bi < WI; ++bi)
                 *(LDS_PTR(f32x4))st_addr(frow, bi * 4 + fq) = acc[bi][jj];
+            if constexpr (SW) {
+                // gate units 0-31 in slots 0-7, the up units in slots 8-15
+                const int rr = lane >> 2, c4 = lane & 3;
+                const f32x4 g0 = *(LDS_PTR(f32x4))st_addr(rr, 2 * c4);
+                const f32x4 g1 = *(LDS_PTR(f32x4))st_addr(rr, 2 * c4 + 1);
+                const f32x4 u0 = *(LDS_PTR(f32x4))st_addr(rr, 8 + 2 * c4);
+                const f32x4 u1 = *(LDS_PTR(f32x4))st_addr(rr, 8 + 2 * c4 + 1);
+                const int64_t m = tm_w + jj * 16 + rr;
+                if (m >= g.M) continue;
+                bf16x8 hv;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float gg = e < 4 ? g0[e] : g1[e - 4], uu = e < 4 ? u0[e] : u1[e - 4];
+                    if (bias) {
+                        gg = gg + bg[e];
+                        uu = uu + bu[e];
+                    }
+                    hv[e] = (__bf16)(silu_f32(gg) * uu);
+                }
+                __bf16 *row = (__bf16 *)g.C + cbase + m * g.ldc;
+                if (vec_store && nsw + 8 <= g.N) {
+                    __builtin_nontemporal_store(hv, (bf16x8 *)(row + nsw));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (nsw + e < g.N) row[nsw + e] = hv[e];
+                }
+                continue;
+            }
             if constexpr (OUT == OUT_F32) {
                 constexpr int LPR4 = 4 * WI;        // lanes per staged row, 4 fp32 each
                 constexpr int RPP4 = 64 / LPR4;     // rows per pass
@@ -365,7 +421,8 @@ hipError_t launch_gemm_narrow(const GemmArgs &g, int out_type, const GemmExtra *
     if (g.M == 0 || g.N == 0 || g.P == 0) return hipSuccess;
     GemmExtra ex{};
     if (exp) ex = *exp;
-    if (ex.act != ACT_NONE || ex.x_rows > 0 || (out_type != OUT_BF16 && ex.bias))
+    const bool sw = ex.act == ACT_SWIGLU;
+    if ((ex.act != ACT_NONE && !sw) || ex.x_rows > 0 || (out_type != OUT_BF16 && (ex.bias || sw)))
         return hipErrorInvalidValue;
     // 128-row tiles when they fit in one pass over the CUs, else 256-row.
     // Same-box A/B, 8 shards, us after a read-only 1 GiB cache flush / warm,
@@ -374,7 +431,7 @@ hipError_t launch_gemm_narrow(const GemmArgs &g, int out_type, const GemmExtra *
     // M = 256, 8192 -> 10240: 83.9 / 62.0 vs 110.7 / 88.6; M = 200,
     // 4096 -> 14336: 49.0 / 41.6 vs 57.6 / 49.4.  Bitwise equal.
     const int cus = device_cu_count();
-    const int64_t tn128 = (g.N + 127) / 128;
+    const int64_t tn128 = sw ? (g.N + 63) / 64 : (g.N + 127) / 128;   // tiles of 128 W rows
     const int FM = ((g.M + 127) / 128) * tn128 * g.P <= cus ? 128 : 256;
     const int64_t tm = (g.M + FM - 1) / FM;
     // 64-column tiles where 128 x 128 ones would fill at most half of the
@@ -383,8 +440,8 @@ hipError_t launch_gemm_narrow(const GemmArgs &g, int out_type, const GemmExtra *
     // M = 128 70.1 / 51.6 vs 81.5 / 55.8; M = 128, 4096 -> 4096 36.9 / 27.3
     // vs 43.3 / 30.9; row partials M = 128, 8192 -> 2048 15.0 / 12.2 vs
     // 17.7 / 14.4.  Bitwise equal.
-    const int TN = (FM == 128 && 2 * tm * tn128 * g.P <= cus) ? 64 : 128;
-    const int64_t tn = (g.N + TN - 1) / TN;
+    const int TN = (!sw && FM == 128 && 2 * tm * tn128 * g.P <= cus) ? 64 : 128;
+    const int64_t tn = sw ? tn128 : (g.N + TN - 1) / TN;
     const int64_t T = tm * tn * g.P;
     if (T > 0x7FFFFFFFll) return hipErrorInvalidConfiguration;
     NarrowSched ts;
@@ -397,20 +454,26 @@ hipError_t launch_gemm_narrow(const GemmArgs &g, int out_type, const GemmExtra *
     const int vw = out_type == OUT_BF16 ? 8 : 4;
     const int vec = g.ldc % vw == 0 && g.c_shard % vw == 0 && aligned16(g.C);
     const __bf16 *bias = (const __bf16 *)ex.bias;
-    if (TN == 64) {
-        if (out_type == OUT_BF16)
-            gemm_narrow_kernel<OUT_BF16, 128, 64><<<dim3(grid), dim3(256), 0, s>>>(g, ts, bias, ex.bias_shard, vec);
+    const int64_t uo = ex.up_off;
+    if (sw) {
+        if (FM == 128)
+            gemm_narrow_kernel<OUT_BF16, 128, 128, true><<<dim3(grid), dim3(256), 0, s>>>(g, ts, bias, ex.bias_shard, vec, uo);
         else
-            gemm_narrow_kernel<OUT_F32, 128, 64><<<dim3(grid), dim3(256), 0, s>>>(g, ts, nullptr, 0, vec);
+            gemm_narrow_kernel<OUT_BF16, 256, 128, true><<<dim3(grid), dim3(512), 0, s>>>(g, ts, bias, ex.bias_shard, vec, uo);
+    } else if (TN == 64) {
+        if (out_type == OUT_BF16)
+            gemm_narrow_kernel<OUT_BF16, 128, 64><<<dim3(grid), dim3(256), 0, s>>>(g, ts, bias, ex.bias_shard, vec, 0);
+        else
+            gemm_narrow_kernel<OUT_F32, 128, 64><<<dim3(grid), dim3(256), 0, s>>>(g, ts, nullptr, 0, vec, 0);
     } else if (FM == 128) {
         if (out_type == OUT_BF16)
-            gemm_narrow_kernel<OUT_BF16, 128, 128><<<dim3(grid), dim3(256), 0, s>>>(g, ts, bias, ex.bias_shard, vec);
+            gemm_narrow_kernel<OUT_BF16, 128, 128><<<dim3(grid), dim3(256), 0, s>>>(g, ts, bias, ex.bias_shard, vec, 0);
         else
-            gemm_narrow_kernel<OUT_F32, 128, 128><<<dim3(grid), dim3(256), 0, s>>>(g, ts, nullptr, 0, vec);
+            gemm_narrow_kernel<OUT_F32, 128, 128><<<dim3(grid), dim3(256), 0, s>>>(g, ts, nullptr, 0, vec, 0);
     } else if (out_type == OUT_BF16) {
-        gemm_narrow_kernel<OUT_BF16, 256, 128><<<dim3(grid), dim3(512), 0, s>>>(g, ts, bias, ex.bias_shard, vec);
+        gemm_narrow_kernel<OUT_BF16, 256, 128><<<dim3(grid), dim3(512), 0, s>>>(g, ts, bias, ex.bias_shard, vec, 0);
     } else {
-        gemm_narrow_kernel<OUT_F32, 256, 128><<<dim3(grid), dim3(512), 0, s>>>(g, ts, nullptr, 0, vec);
+        gemm_narrow_kernel<OUT_F32, 256, 128><<<dim3(grid), dim3(512), 0, s>>>(g, ts, nullptr, 0, vec, 0);
     }
     return hipGetLastError();
 }

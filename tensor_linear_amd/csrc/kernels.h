@@ -67,8 +67,9 @@ bool gemm_tile_supported(const GemmArgs &g, const GemmExtra *ex);
 // Narrow tiles for launches whose 256 x 256 tiles would fill at most half of
 // the CUs: 128 x 128 (four waves) when those fit in one pass over the CUs,
 // 128 x 64 when they would fill at most half of it, else 256 x 128 (eight
-// waves, two per SIMD); no gated unit or token slices, and the bias only
-// with bf16 output.  Bitwise the same results as the tile kernel.
+// waves, two per SIMD); no token slices, and the bias and the gated unit
+// (on 128 W rows: 64 outputs per tile) only with bf16 output.  Bitwise the
+// same results as the tile kernel.
 hipError_t launch_gemm_narrow(const GemmArgs &g, int out_type, const GemmExtra *ex,
                               hipStream_t s);
 

@@ -87,9 +87,10 @@ hipError_t run_gemm(const GemmArgs &g, int32_t dtype, int out_type, const GemmEx
             // 82.9 vs 168.9 / 133.3 us; M = 256, 4096 -> 28672: 114.7 / 53.1
             // vs 123.7 / 74.9 us (its 128 x 128 form is faster again where
             // those tiles fit in one pass).
-            const bool plain = !ex || (ex->act == ACT_NONE && ex->x_rows == 0 &&
-                                       (out_type == OUT_BF16 || !ex->bias));
-            const int64_t t256 = ((g.M + 255) / 256) * ((g.N + 255) / 256) * g.P;
+            const bool sw = ex && ex->act == ACT_SWIGLU;
+            const bool plain = !ex || (ex->x_rows == 0 && (out_type == OUT_BF16 || (!ex->bias && !sw)));
+            // the tile kernel's tiles: 256 W rows, 128 outputs with the gated unit
+            const int64_t t256 = ((g.M + 255) / 256) * ((g.N + (sw ? 127 : 255)) / (sw ? 128 : 256)) * g.P;
             if (plain && 2 * t256 <= device_cu_count()) return launch_gemm_narrow(g, out_type, ex, s);
             return launch_gemm_tile(g, out_type, ex, s);
         }

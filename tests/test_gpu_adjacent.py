@@ -210,11 +210,33 @@ SWIGLU = [
     # (M, K, I, P, dtype, with_bias)
     (9, 256, 2 * 24, 2, torch.bfloat16, True),     # skinny (16 gate + 16 up rows per workgroup)
     (40, 256, 2 * 24, 2, torch.bfloat16, False),   # skinny, two m-blocks
-    (300, 128, 2 * 136, 2, torch.bfloat16, True),  # tile, ragged M, I/P = 136 (ragged 128 block)
-    (512, 128, 4 * 128, 4, torch.bfloat16, False),  # tile, whole tiles
+    (300, 128, 2 * 136, 2, torch.bfloat16, True),  # narrow 128-row tiles, ragged M, I/P = 136
+    (512, 128, 4 * 128, 4, torch.bfloat16, False),  # narrow 128-row tiles, whole tiles
+    (1024, 128, 8 * 512, 8, torch.bfloat16, True),  # narrow 256-row tiles
+    (1100, 128, 16 * 256, 16, torch.bfloat16, True),  # 256 x 256 tile kernel (160 tiles), ragged M
     (300, 128, 2 * 132, 2, torch.bfloat16, True),  # I/P = 132: up offset not a multiple of 8 -> generic
     (5, 10, 2 * 3, 2, torch.float32, True),        # fp32 generic
 ]
+
+
+def test_swiglu_kernels_agree_on_rows():
+    """The gated unit on the 256 x 256 tile kernel and on both narrow tile
+    shapes: the first rows of a longer launch equal a shorter launch bit for
+    bit (an output row depends only on its X row, and these kernels add K in
+    the same order), on N(0,1) x N(0, 0.02^2) data with the bias."""
+    P, On, K = 16, 256, 256
+    N = 2 * On * P
+    X = bf16_dev(synth.normal_bf16(71, (1100, K)))
+    W = bf16_dev(synth.normal_bf16(72, (N, K), 0.02))
+    b = bf16_dev(synth.normal_bf16(73, (N,), 0.02))
+    outs = {}
+    for M in (1100, 600, 300):   # 160 tiles of 256 x 256; narrow 256-row; narrow 128-row
+        print(f"swiglu rows M={M}", flush=True)
+        Y = torch.full((M, On * P), float("nan"), dtype=torch.bfloat16, device=DEV)
+        tl.tp_linear_column_ex(X[:M], W, Y, P, bias=b, act=tl.TP_ACT_SWIGLU)
+        outs[M] = bits(Y)
+    assert np.array_equal(outs[600], outs[1100][:600])
+    assert np.array_equal(outs[300], outs[1100][:300])
 
 
 @pytest.mark.parametrize("case", range(len(SWIGLU)))
@@ -440,10 +462,11 @@ def test_embedding_out_of_range_ids():
 # ---------------------------------------------------------------------------
 
 GUARD = [
-    # (M, K, N, P, act): tile path with whole and ragged tiles, skinny, generic
+    # (M, K, N, P, act): narrow and tile paths with whole and ragged tiles, skinny, generic
     (300, 128, 2 * 272, 2, tl.TP_ACT_NONE),
     (300, 128, 2 * 272, 2, tl.TP_ACT_SWIGLU),
     (512, 128, 4 * 256, 4, tl.TP_ACT_SWIGLU),
+    (1100, 128, 16 * 512, 16, tl.TP_ACT_SWIGLU),
     (9, 256, 2 * 48, 2, tl.TP_ACT_SWIGLU),
     (9, 256, 2 * 48, 2, tl.TP_ACT_NONE),
     (70, 40, 3 * 12, 3, tl.TP_ACT_SWIGLU),
