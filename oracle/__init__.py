@@ -22,7 +22,7 @@ Every step below is the plain definition from the pages, slow and explicit:
     "模型并行", "Sequence Parallel": the row result may instead be
     reduce-scattered over tokens and later all-gathered.
 
-Readings where the pages leave a point open (each listed in the design doc):
+Readings where the pages leave a point open:
   * the P partial results are summed in ascending shard order, left to right;
   * the reduce-scatter splits the token dim (dim 0) into P equal row blocks,
     block j going to shard j;
