@@ -166,8 +166,10 @@ tp_status tp_linear_column(const void *X, int64_t ldx, const void *W, int64_t ld
  *   shard partials of its output tile in ascending order and adds them into
  *   a running fp32 sum, so no partial reaches memory and the workspace is
  *   not touched.  Kernels exist for bf16 operands (16-byte aligned, leading
- *   dims and shard offsets multiples of 8) with 1 <= M <= 48, or with K/P a
- *   multiple of 64 and at most 2048 (at most 3584 when M*N >= 4096*4096);
+ *   dims and shard offsets multiples of 8) with 1 <= M <= 32 (up to 48 when
+ *   K/P > 4096 or the P partials span at most CUs/2 tiles of 128 x 128), or
+ *   with K/P a multiple of 64 and at most 2048 (at most 3584 when M*N >=
+ *   4096*4096);
  *   they are used where they measured faster: for M <= 16 when N >= 32 x the
  *   GPU's CU count and K/P >= 2048, or N is smaller and K/P <= 1024; for
  *   M > 64 when the output has at least CUs * min(1, (K/P + 512) / 2048)

@@ -69,8 +69,28 @@ int64_t view_stride(int64_t rows, int64_t cols, int64_t ld, int32_t kind, int32_
     return stride;
 }
 
+// Whether a bf16 shard GEMM takes the skinny kernel: up to 32 tokens, and up
+// to 48 where the tile kernels do no better -- a shard K above 4096 (the
+// skinny kernel's longer runs per workgroup pay off) or so few 128-row tiles
+// over all P shards that they would fill at most half of the CUs.  Same box,
+// 8 shards, us after a read-only flush / warm, 33-48 tokens, skinny vs tiles:
+// column 4096 -> 28672 66.4-68.3 / 56.1-57.4 vs 59.4-62.3 / 38.6-39.2, 8192
+// -> 28672 106.0-109.9 / 105.5-108.5 vs 115.4-119.6 / 114.8-118.5; row
+// partials + fold 14336 -> 4096 41.2-42.7 / 37.2-37.3 vs 31.2-31.4 / 26.4-26.6,
+// 28672 -> 8192 118.2-136.7 / 113.3-117.5 vs 100.9-114.1 / 101.0-104.0.  The
+// tile count uses all shards' columns together, so a column layer takes the
+// same kernel family whatever P is (and the same bits).
+bool skinny_takes(const GemmArgs &g, const GemmExtra *ex) {
+    if (!gemm_skinny_supported(g, ex)) return false;
+    if (g.M <= 32 || g.K > 4096 || !gemm_tile_supported(g, ex)) return true;
+    const int64_t cols = ex && ex->act == ACT_SWIGLU ? 64 : 128;   // outputs per 128 W rows
+    const int64_t t128 = ((g.M + 127) / 128) * ((g.N * g.P + cols - 1) / cols);
+    return 2 * t128 <= device_cu_count();
+}
+
 // Run one grouped shard GEMM with the best kernel that takes it.
-// Decode-shaped bf16 problems (M <= 48) stream W with the skinny kernel;
+// Decode-shaped bf16 problems (up to 32 or 48 tokens, see skinny_takes)
+// stream W with the skinny kernel;
 // aligned bf16 problems use the 256x256 MFMA tile kernel, or its narrow
 // forms (128x128, or 256x128 with two waves per SIMD) when the 256x256
 // tiles would fill at most half of the CUs; everything else (fp32, odd K,
@@ -78,7 +98,7 @@ int64_t view_stride(int64_t rows, int64_t cols, int64_t ld, int32_t kind, int32_
 hipError_t run_gemm(const GemmArgs &g, int32_t dtype, int out_type, const GemmExtra *ex,
                     hipStream_t s) {
     if (dtype == TP_BF16) {
-        if (gemm_skinny_supported(g, ex)) return launch_gemm_skinny(g, out_type, nullptr, ex, s);
+        if (skinny_takes(g, ex)) return launch_gemm_skinny(g, out_type, nullptr, ex, s);
         if (gemm_tile_supported(g, ex)) {
             // Few 256 x 256 tiles (short prompts): the narrow kernel.  Its
             // 256 x 128 form against the 256 x 256 tiles, same-box times, 8
@@ -356,7 +376,7 @@ tp_status plan_row(const void *X, int64_t ldx, const void *W, int64_t ldw, const
     // Fold inside the GEMM where a kernel takes the shape and that is the
     // faster way, or the override asks for it, or the partials would not fit.
     const bool any_fold = row_fold_in_gemm_forced() || partials_bytes(M, N, P) > ws_cap;
-    if (mode == TP_ROW_FUSED && dtype == TP_BF16 && gemm_skinny_supported(g, nullptr) &&
+    if (mode == TP_ROW_FUSED && dtype == TP_BF16 && skinny_takes(g, nullptr) &&
         (any_fold || skinny_fold_faster(M, N, Ks))) {
         p.f.Y = Y; p.f.ldy = ldy; p.f.out_type = p.out;
         p.path = RowPlan::SKINNY_FOLD;

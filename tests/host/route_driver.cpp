@@ -23,7 +23,7 @@ bool gemm_skinny_supported(const GemmArgs &g, const GemmExtra *) { return g.M >=
 bool gemm_rowfold_supported(const GemmArgs &g, const ReduceArgs &r) {
     return g.K % 64 == 0 && !(r.slice_rows < g.M && r.slice_rows % 256 != 0);
 }
-bool gemm_tile_supported(const GemmArgs &, const GemmExtra *) { std::abort(); }
+bool gemm_tile_supported(const GemmArgs &g, const GemmExtra *) { return g.K % 64 == 0; }
 hipError_t launch_gemm_tile(const GemmArgs &, int, const GemmExtra *, hipStream_t) { std::abort(); }
 hipError_t launch_gemm_narrow(const GemmArgs &, int, const GemmExtra *, hipStream_t) { std::abort(); }
 hipError_t launch_gemm_skinny(const GemmArgs &, int, const FoldArgs *, const GemmExtra *, hipStream_t) {
@@ -113,7 +113,7 @@ int main() {
     EXPECT(TP_ROW_SCATTER, 16, 8192, 3584, 8, PF);     // the decode kernel has no scatter form
     // Partials that would not fit the caller's workspace: every shape a
     // fused kernel takes folds inside the GEMM.
-    EXPECT(TP_ROW_FUSED, 48, 32768, 64, 8, SK, (size_t)32 << 20);
+    EXPECT(TP_ROW_FUSED, 48, 32768, 4160, 8, SK, (size_t)32 << 20);   // K/P > 4096: skinny
     EXPECT(TP_ROW_FUSED, 64, 32768, 64, 8, RF, (size_t)32 << 20);
     EXPECT(TP_ROW_FUSED, 2048, 1024, 1024, 8, RF, (size_t)32 << 20);
     EXPECT(TP_ROW_FUSED, 2048, 1024, 1024, 8, PF, (size_t)64 << 20);   // they fit
@@ -121,7 +121,9 @@ int main() {
     EXPECT(TP_ROW_SUM, 2048, 1024, 1024, 8, PF, (size_t)32 << 20);     // TP_ROW_SUM never folds inside
     // TPLINEAR_ROW_FOLD=gemm: the same, whatever the sizes.
     setenv("TPLINEAR_ROW_FOLD", "gemm", 1);
-    EXPECT(TP_ROW_FUSED, 48, 4096, 512, 8, SK);
+    EXPECT(TP_ROW_FUSED, 48, 512, 512, 8, SK);      // few tiles: skinny
+    EXPECT(TP_ROW_FUSED, 32, 4096, 512, 8, SK);
+    EXPECT(TP_ROW_FUSED, 48, 4096, 512, 8, RF);     // 256 tiles of 128 rows: the tile order
     EXPECT(TP_ROW_FUSED, 64, 4096, 512, 8, RF);
     EXPECT(TP_ROW_FUSED, 16, 8192, 1024, 8, SK);
     EXPECT(TP_ROW_FUSED, 65, 4096, 64, 8, RF);
