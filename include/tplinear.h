@@ -169,9 +169,9 @@ tp_status tp_linear_column(const void *X, int64_t ldx, const void *W, int64_t ld
  *   dims and shard offsets multiples of 8) with 1 <= M <= 32 (up to 48 when
  *   K/P > 4096 or the P partials span at most CUs/2 tiles of 128 x 128), or
  *   with K/P a multiple of 64 and at most 2048 (at most 3584 when M*N >=
- *   4096*4096);
- *   they are used where they measured faster: for M <= 16 when N >= 32 x the
- *   GPU's CU count and K/P >= 2048, or N is smaller and K/P <= 1024; for
+ *   4096*4096); they are used where they measured faster: for M <= 16 when
+ *   N >= 32 x the GPU's CU count and K/P >= 2048, or N is smaller and
+ *   K/P <= 1024; for
  *   M > 64 when the output has at least CUs * min(1, (K/P + 512) / 2048)
  *   tiles of 256 x 128.  Other shapes run the TP_ROW_SUM sequence in the
  *   workspace, which is therefore always required.  With the environment
