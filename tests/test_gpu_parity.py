@@ -97,6 +97,7 @@ ALIGNED = [
     (1, 512, 64, 8),
     (17, 256, 192, 4),             # skinny, two m-blocks, ragged M
     (48, 1024, 512, 2),            # skinny, three m-blocks
+    (40, 512, 4096 * 8, 8),        # 33-48 tokens on the tile order: column 128 x 128 tiles, row 256 x 256
     (64, 1024, 512, 2),            # 128 x 64 tiles, 64 tokens
     (65, 512, 512, 2),             # few tiles: 128 x 64 tiles, mostly-empty M tile
     (300, 512, 2 * 300, 2),        # 128 x 64 tiles, ragged M and N/P = 300
