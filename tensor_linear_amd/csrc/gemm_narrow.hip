@@ -1,9 +1,10 @@
 // Column shard GEMM (and row partials) on narrow output tiles, for launches
 // whose 256 x 256 tiles would fill at most half of the CUs ("模型并行",
 // "Tensor Parallel": the per-shard products Y_i = X W_i and X_i W_i).  Each
-// wave owns a 64 x 64 block of 4 x 4 v_mfma_f32_16x16x32_bf16 blocks, with
-// the instruction and the K order of the 256 x 256 tile kernel, so every
-// output is bitwise the same.  Three tile shapes:
+// wave owns a 64 x 64 block of 4 x 4 v_mfma_f32_16x16x32_bf16 blocks (64 x
+// 32 in the 64-column tiles), with the instruction and the K order of the
+// 256 x 256 tile kernel, so every output is bitwise the same.  Three tile
+// shapes:
 //  - 128 x 128 tiles, four waves in a 2 x 2 grid, when they fit in one pass
 //    over the CUs (up to 128 tokens, and up to 256 when the N side is short):
 //    no MFMA work on rows past M, twice the workgroups of 256-row tiles
@@ -27,9 +28,8 @@
 // substep-1 fragments and issues all of step it+2's loads (6 per wave with
 // 256 rows, 8 with 128, 6 with 64 columns) into the stage step it-1 freed;
 // then the step's one barrier; during substep 1 it reads the next step's
-// substep-0 fragments.  Persistent
-// workgroups walk an XCD-contiguous range of (shard, tile) pairs; the K
-// pipeline runs across tiles.
+// substep-0 fragments.  Persistent workgroups walk an XCD-contiguous range
+// of (shard, tile) pairs; the K pipeline runs across tiles.
 #include "kernels.h"
 
 namespace tpl {
