@@ -1,5 +1,5 @@
-// Host-only driver: which way the row modes fold (tpl::plan_row), for a GPU
-// of 256 CUs.  TP_ROW_FUSED and TP_ROW_SCATTER give the bits of TP_ROW_SUM
+// Host-only driver: which kernel a column layer takes, and which way the
+// row modes fold (tpl::plan_row), for a GPU of 256 CUs.  TP_ROW_FUSED and TP_ROW_SCATTER give the bits of TP_ROW_SUM
 // whichever way they fold, so the choice is by speed: the fused decode
 // kernel for M <= 16 where its grid fills the CUs with 32 output columns
 // per workgroup and K/P >= 2048, or where it does not and K/P <= 1024; the
@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstdint>
+#include <cstring>
 
 #include "tplinear.h"
 #include "kernels.h"
@@ -24,10 +25,19 @@ bool gemm_rowfold_supported(const GemmArgs &g, const ReduceArgs &r) {
     return g.K % 64 == 0 && !(r.slice_rows < g.M && r.slice_rows % 256 != 0);
 }
 bool gemm_tile_supported(const GemmArgs &g, const GemmExtra *) { return g.K % 64 == 0; }
-hipError_t launch_gemm_tile(const GemmArgs &, int, const GemmExtra *, hipStream_t) { std::abort(); }
-hipError_t launch_gemm_narrow(const GemmArgs &, int, const GemmExtra *, hipStream_t) { std::abort(); }
+// The column GEMM's launches are recorded, not run.
+const char *last_launch = "";
+hipError_t launch_gemm_tile(const GemmArgs &, int, const GemmExtra *, hipStream_t) {
+    last_launch = "tile";
+    return hipSuccess;
+}
+hipError_t launch_gemm_narrow(const GemmArgs &, int, const GemmExtra *, hipStream_t) {
+    last_launch = "narrow";
+    return hipSuccess;
+}
 hipError_t launch_gemm_skinny(const GemmArgs &, int, const FoldArgs *, const GemmExtra *, hipStream_t) {
-    std::abort();
+    last_launch = "skinny";
+    return hipSuccess;
 }
 hipError_t launch_gemm_rowfold(const GemmArgs &, const ReduceArgs &, hipStream_t) { std::abort(); }
 hipError_t launch_gemm_generic(const GemmArgs &, int, int, const GemmExtra *, hipStream_t) { std::abort(); }
@@ -64,6 +74,22 @@ static void expect(int line, int32_t mode, int64_t M, int64_t N, int64_t Ks, int
     }
 }
 #define EXPECT(...) expect(__LINE__, __VA_ARGS__)
+
+// Which kernel a bf16 column layer [M, K] x [N, K]^T over P shards takes.
+static void expect_col(int line, int64_t M, int64_t N, int64_t K, int32_t P, const char *want,
+                       int32_t act = TP_ACT_NONE) {
+    void *F = reinterpret_cast<void *>(0x1000);
+    tpl::last_launch = "";
+    const int64_t On = act == TP_ACT_SWIGLU ? N / 2 : N;
+    const tp_status st = tp_linear_column_ex(F, nullptr, K, F, K, nullptr, F, On, TP_Y_CONCAT, act,
+                                             M, N, K, P, TP_BF16, nullptr);
+    if (st != TP_OK || std::strcmp(tpl::last_launch, want) != 0) {
+        std::fprintf(stderr, "line %d: column M=%lld N=%lld K=%lld P=%d act %d: status %d kernel %s, want %s\n",
+                     line, (long long)M, (long long)N, (long long)K, P, act, (int)st, tpl::last_launch, want);
+        ++failures;
+    }
+}
+#define EXPECT_COL(...) expect_col(__LINE__, __VA_ARGS__)
 
 int main() {
     const Path PART = tpl::RowPlan::PARTIAL, SK = tpl::RowPlan::SKINNY_FOLD, RF = tpl::RowPlan::ROWFOLD,
@@ -135,6 +161,26 @@ int main() {
     setenv("TPLINEAR_ROW_FOLD", "auto", 1);          // any other value: the library's choice
     EXPECT(TP_ROW_FUSED, 64, 4096, 512, 8, PF);
     unsetenv("TPLINEAR_ROW_FOLD");
+
+    // The column GEMM: skinny up to 32 tokens, and up to 48 for K > 4096 or
+    // when 128-row tiles over all shards would fill at most half of the CUs;
+    // the narrow kernel when 256 x 256 tiles would fill at most half of them.
+    EXPECT_COL(16, 28672, 8192, 8, "skinny");
+    EXPECT_COL(32, 28672, 4096, 8, "skinny");
+    EXPECT_COL(33, 28672, 4096, 8, "narrow");     // 224 tiles of 128 rows
+    EXPECT_COL(48, 28672, 4096, 8, "narrow");
+    EXPECT_COL(48, 28672, 4096, 1, "narrow");     // the same family whatever P is
+    EXPECT_COL(48, 28672, 8192, 8, "skinny");     // K > 4096
+    EXPECT_COL(48, 10240, 4096, 8, "skinny");     // 80 tiles of 128 rows
+    EXPECT_COL(49, 10240, 8192, 8, "narrow");
+    EXPECT_COL(48, 65536, 4096, 8, "tile");       // 256 tiles of 256 x 256
+    EXPECT_COL(256, 28672, 4096, 8, "narrow");    // 112 tiles of 256 x 256
+    EXPECT_COL(512, 28672, 4096, 8, "tile");      // 224
+    EXPECT_COL(4096, 28672, 4096, 8, "tile");
+    EXPECT_COL(40, 28672, 4096, 8, "narrow", TP_ACT_SWIGLU);   // gated unit: 64 outputs per 128 W rows
+    EXPECT_COL(40, 8192, 4096, 8, "skinny", TP_ACT_SWIGLU);
+    EXPECT_COL(256, 28672, 4096, 8, "narrow", TP_ACT_SWIGLU);  // 112 tiles of 256 rows x 128 outputs
+    EXPECT_COL(512, 28672, 4096, 8, "tile", TP_ACT_SWIGLU);    // 224
     if (failures) {
         std::fprintf(stderr, "%d failures\n", failures);
         return 1;

@@ -57,9 +57,10 @@ def test_launch_offsets_follow_layout(tmp_path):
 
 @pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not found")
 def test_row_fold_routing(tmp_path):
-    """Which way TP_ROW_FUSED / TP_ROW_SCATTER fold (inside the GEMM or
-    partials + fold, the same bits either way) for a GPU of 256 CUs, with
-    the library's own choice, TPLINEAR_ROW_FOLD=gemm, and a workspace the
+    """Which kernel a column layer takes (skinny, narrow or tile), and which
+    way TP_ROW_FUSED / TP_ROW_SCATTER fold (inside the GEMM or partials +
+    fold, the same bits either way), for a GPU of 256 CUs, with the
+    library's own choice, TPLINEAR_ROW_FOLD=gemm, and a workspace the
     partials would not fit (tests/host/route_driver.cpp)."""
     inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROOT, "tensor_linear_amd", "csrc"),
            "-I", "/opt/rocm/include", "-D__HIP_PLATFORM_AMD__"]
